@@ -1,0 +1,189 @@
+/*
+ * gptq.h — C ABI of the MI355X (gfx950) GPTQ layer quantizer.
+ *
+ * The library quantizes one linear layer W [d_out, d_in] (or a batch of independent
+ * layers, e.g. the experts of a mixture-of-experts block) to a uniform 2..8-bit grid by
+ * the GPTQ procedure:
+ *
+ *   minimise || W X - What X ||_F^2 over grid-restricted What
+ *     ("04 — GPTQ: Hessian-Weighted Rounding, the OBS Lineage, and Why It Still Ships",
+ *      section 1; "GPTQ Architecture, in depth", "The algorithm on one page")
+ *
+ * in four calls that follow the pages' split of the work:
+ *   gptq_accumulate_hessian  H += 2 X^T X per calibration batch
+ *   gptq_prepare_hinv        dead inputs, ActOrder, damping, U with H_p^-1 = U^T U
+ *   gptq_quantize_layer      blocked column sweep with lazy trailing updates
+ *   gptq_pack_int4           checkpoint tensors (qweight, qzeros, fp16 scales)
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library never
+ *     allocates or frees memory; scratch memory comes in through `workspace`, whose
+ *     required size is returned by gptq_workspace_size().  Nothing is retained between
+ *     calls.
+ *   - Every call enqueues its kernels on `stream` and returns without waiting, except
+ *     gptq_prepare_hinv, which waits for its own kernels to read the factorisation
+ *     status.  Outputs are valid once the stream reaches the end of the call's work.
+ *   - Arrays are dense row-major; "stride" arguments count ELEMENTS of the array's own
+ *     type.  `batch` independent problems are addressed by the batch strides.
+ *   - Errors are returned, never printed; on an error the outputs are unspecified.
+ *     Argument errors are detected before anything is enqueued.
+ *   - Calls on different streams that share a workspace race; calls on one stream do
+ *     not.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = -1, /* bad sizes, strides, null pointers or parameters          */
+  GPTQ_ERR_NOT_SPD = -2,     /* the damped Hessian has no Cholesky factor                 */
+  GPTQ_ERR_HIP = -3,         /* a HIP runtime call failed                                  */
+  GPTQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than gptq_workspace_size()   */
+  GPTQ_ERR_UNSUPPORTED = -5  /* valid request outside what this build implements          */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
+
+/* Quantizer knobs ("GPTQ Architecture, in depth", "The algorithm in code" and
+ * "Groups, act-order and other knobs"; damping: "Same Ruler, Smarter Placement:
+ * GPTQ", 1.6).
+ *   bits        2..8; codes lie in [0, 2^bits - 1]
+ *   group_size  -1: one asymmetric min-max grid per row, fitted once on the whole row;
+ *               otherwise a divisor of 128 that divides d_in: the grid of each group of
+ *               consecutive columns IN PROCESSING ORDER is refitted on the current
+ *               (already compensated) weights when the sweep reaches its first column
+ *   block_size  columns per lazy batch; must be 128
+ *   damp        lambda = damp * mean(diag H) is added to the diagonal (>= 0)
+ *   act_order   nonzero: process columns by descending Hessian diagonal            */
+typedef struct {
+  int bits;
+  int group_size;
+  int block_size;
+  float damp;
+  int act_order;
+} gptq_params;
+
+/* Which call a workspace is sized for. */
+typedef enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2 } gptq_ws_call;
+
+/*
+ * Hessian accumulation — "Same Ruler, Smarter Placement: GPTQ", 1.4 (H = 2 X X^T, the
+ * same matrix for every output row) and "GPTQ Architecture, in depth", "The algorithm
+ * in code" (accumulated over calibration batches).
+ *
+ * For every problem e < batch:
+ *   H[e]        += 2 * X[e]^T X[e]          fp32, full symmetric [d_in, d_in]
+ *   diag_key[e] += 2 * sum_t X[e][t,:]^2    fp64 [d_in]; the exact-to-fp64 diagonal,
+ *                                           used for the dead-input test, the ActOrder
+ *                                           order and the damping mean
+ *   n_seen[e]   += n_tokens                 int64
+ * X[e] is token-major [n_tokens, d_in] with row stride ldx (>= d_in) and batch stride
+ * batch_stride_x; dtype bf16, fp16 or fp32 (products are exact in fp32, sums are fp32;
+ * the fp64 key sums the same products in fp64).  H[e] starts at H + e*batch_stride_h
+ * (>= d_in*d_in).  Zero H, diag_key and n_seen before the first batch.  n_tokens may be
+ * 0 (no-op) and need not be a multiple of any tile.  Requires d_in % 8 == 0.
+ */
+gptq_status gptq_accumulate_hessian(int batch, int d_in, int64_t n_tokens, gptq_dtype x_dtype,
+                                    const void* X, int64_t ldx, int64_t batch_stride_x,
+                                    float* H, int64_t batch_stride_h, double* diag_key,
+                                    int64_t* n_seen, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * Inverse-Hessian factor — "GPTQ Architecture, in depth", "The algorithm in code"
+ * (dead inputs, act-order, damping) and "Same Ruler, Smarter Placement: GPTQ", 1.6,
+ * 1.7 and 1.9.
+ *
+ * For every problem e:
+ *   dead[c] = (diag_key[c] == 0)            uint8 [d_in]; such inputs get H_cc = 1
+ *   perm    = columns by descending key (dead inputs count as key 1), ties by ascending
+ *             index; the identity when act_order == 0            int32 [d_in]
+ *   H_p     = H[perm][:, perm] with diagonal key[perm] + lambda,
+ *             lambda = damp * mean(key)  (key after the dead-input fix, fp64)
+ *   U       = the upper-triangular factor with positive diagonal and H_p^-1 = U^T U,
+ *             fp32 [d_in, d_in] in processing (permuted) order; the strictly lower part
+ *             is written as zero.
+ * The off-diagonal of H_p comes from the fp32 H (only its lower triangle is read); the
+ * diagonal from diag_key.  H is not modified.  Computed through H_p = Ut Ut^T (Ut upper:
+ * the Cholesky factor of the index-reversed H_p) and U = Ut^-1; positive-diagonal
+ * factors are unique, so this is the same U as the pages' chol / cholesky_inverse /
+ * chol route.  Returns GPTQ_ERR_NOT_SPD (after waiting for the stream) when a pivot is
+ * not positive or not finite; the caller may retry with a larger damp.
+ * Requires d_in % 128 == 0.
+ */
+gptq_status gptq_prepare_hinv(int batch, int d_in, const float* H, int64_t batch_stride_h,
+                              const double* diag_key, const gptq_params* p, float* U,
+                              int64_t batch_stride_u, int32_t* perm, uint8_t* dead,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Column sweep — "Same Ruler, Smarter Placement: GPTQ", 1.5 (Steps 1-3), 1.7 (rows of
+ * U), 1.8 (lazy batch update, block 128); "GPTQ Architecture, in depth", "The algorithm
+ * in code" (min-max grid, in-block updates, lazy update, undoing the permutation).
+ *
+ * For every problem e, with W_p = W[:, perm] in fp32 and dead columns zeroed:
+ *   for each column j in processing order:
+ *     at a group start: scale = max((hi - lo) / maxq, 1e-8), zero = rne(-lo / scale)
+ *       with lo = min(0, min W_p[r, group]), hi = max(0, max W_p[r, group]) per row
+ *     code = clamp(rne(W_p[r, j] / scale) + zero, 0, maxq)
+ *     err  = (W_p[r, j] - scale * (code - zero)) / U[j, j]
+ *     W_p[r, later columns of the block] -= err * U[j, later columns of the block]
+ *   after each block of 128 columns: W_p[:, later] -= Err_block @ U[block, later]
+ * Outputs (rne = round half to even):
+ *   codes  uint8 [d_out, d_in] in ORIGINAL column order (batch stride d_out*d_in)
+ *   scales fp32 [n_groups, d_out], zeros uint8 [n_groups, d_out]; n_groups = d_in /
+ *          group_size, or 1 per row; group g holds processing positions [g*gs, (g+1)*gs)
+ *   g_idx  int32 [d_in]: group of each original column (0 per row)
+ * W is bf16, fp16 or fp32 with row stride ldw and batch stride batch_stride_w; U, perm
+ * and dead are the outputs of gptq_prepare_hinv (U batch stride batch_stride_u).
+ * Requires d_in % 128 == 0, d_out >= 1.
+ */
+gptq_status gptq_quantize_layer(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W,
+                                int64_t ldw, int64_t batch_stride_w, const float* U,
+                                int64_t batch_stride_u, const int32_t* perm, const uint8_t* dead,
+                                const gptq_params* p, uint8_t* codes, float* scales,
+                                uint8_t* zeros, int32_t* g_idx, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Checkpoint packing — "04 — GPTQ: ...", section 8, and "GPTQ Architecture, in
+ * depth", "Packing, tooling and serving": eight 4-bit values per int32, element k in
+ * bits [4k, 4k + 4).
+ *   qweight    int32 [d_in/8, d_out]       qweight[i, o] = sum_k codes[o, 8i + k] << 4k
+ *   qzeros     int32 [n_groups, d_out/8]   qzeros[g, i]  = sum_k zeros[g, 8i + k] << 4k
+ *   scales_f16 fp16 bits [n_groups, d_out] round-to-nearest-even of scales
+ * codes / scales / zeros as written by gptq_quantize_layer (values < 16; 3-bit codes are
+ * stored in nibbles too).  Batch strides are the dense sizes of each array.
+ * Requires d_in % 8 == 0 and d_out % 8 == 0.  Values are masked to their low 4 bits;
+ * no range check is made.
+ */
+gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const uint8_t* codes,
+                           const float* scales, const uint8_t* zeros, int32_t* qweight,
+                           int32_t* qzeros, uint16_t* scales_f16, hipStream_t stream);
+
+/* Bytes of workspace the given call needs (0 on invalid arguments).  For
+ * GPTQ_WS_HESSIAN `d_out` is ignored and `n_tokens_hint` is the largest n_tokens per call
+ * (it only sizes the split over tokens); for the other calls it is ignored. */
+size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
+                           int64_t n_tokens_hint, const gptq_params* p);
+
+/* Static description of a status code. */
+const char* gptq_status_string(gptq_status s);
+
+/* Library version, "major.minor.patch". */
+const char* gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

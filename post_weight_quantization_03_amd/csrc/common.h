@@ -1,0 +1,109 @@
+// Internal helpers shared by the HIP translation units of libgptq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gptq.h"
+
+#define GPTQ_HIP_TRY(expr)                         \
+  do {                                             \
+    if ((expr) != hipSuccess) return GPTQ_ERR_HIP; \
+  } while (0)
+
+// A kernel launch: enqueue, then report a failed launch as GPTQ_ERR_HIP.
+#define GPTQ_LAUNCH(kernel, grid, block, lds, stream, ...)                    \
+  do {                                                                       \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);       \
+    if (hipGetLastError() != hipSuccess) return GPTQ_ERR_HIP;                \
+  } while (0)
+
+namespace gptq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 128;  // columns per lazy batch
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
+
+// 16-bit storage types are carried as raw bits; the tag selects the decoding.
+struct BF16 { uint16_t bits; };
+struct F16 { uint16_t bits; };
+template <>
+__device__ __forceinline__ float load_as_f32<BF16>(const BF16* p) { return bf16_to_f32(p->bits); }
+template <>
+__device__ __forceinline__ float load_as_f32<F16>(const F16* p) { return f16_to_f32(p->bits); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Carves consecutive 256-byte aligned regions out of one workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    used = align_up(used, 256);
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+}  // namespace gptq
+
+// Internal entry points of the translation units (host side).
+namespace gptq {
+gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_dtype, const void* X,
+                            int64_t ldx, int64_t bsx, float* H, int64_t bsh, double* diag_key,
+                            int64_t* n_seen, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t hessian_workspace(int batch, int d_in, int64_t n_tokens);
+
+gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, const double* diag_key,
+                            const gptq_params& p, float* U, int64_t bsu, int32_t* perm, uint8_t* dead,
+                            void* ws, size_t ws_bytes, hipStream_t stream, int* not_spd);
+size_t prepare_workspace(int batch, int d_in);
+
+gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W,
+                             int64_t ldw, int64_t bsw, const float* U, int64_t bsu, const int32_t* perm,
+                             const uint8_t* dead, const gptq_params& p, uint8_t* codes, float* scales,
+                             uint8_t* zeros, int32_t* g_idx, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+size_t quantize_workspace(int batch, int d_out, int d_in, const gptq_params& p);
+
+gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uint8_t* codes,
+                         const float* scales, const uint8_t* zeros, int32_t* qweight, int32_t* qzeros,
+                         uint16_t* scales_f16, hipStream_t stream);
+
+// fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C (row-major, batched by blockIdx.z).
+struct GemmArgs {
+  int M, N, K;
+  const float* A; int64_t lda, sA;   // A [M, K]
+  const float* B; int64_t ldb, sB;   // B [K, N], or [N, K] when transB
+  float* C; int64_t ldc, sC;         // C [M, N]
+  float alpha, beta;
+  int transB;
+  int flags;                         // GemmFlags
+  int batch;
+};
+enum GemmFlags {
+  kLowerOut = 1,   // C square: only tiles on or below the diagonal are computed
+  kALower = 2,     // A lower triangular: K range of a row tile ends at its last row
+  kBLower = 4,     // op(B) = B lower triangular (B[k][n] = 0 for k < n): K starts at n0
+  kBtLower = 8,    // op(B) = B^T with B lower (B^T[k][n] = 0 for k > n): K ends at n0 + TN
+};
+gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream);
+}  // namespace gptq

@@ -1,0 +1,186 @@
+// fp32 GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32):
+//   C = alpha * op(A) * op(B) + beta * C,   A [M, K], op(B) = B [K, N] or B^T (B [N, K]).
+//
+// Used for the blocked Cholesky (panel solve as a product with the inverted diagonal
+// block, trailing symmetric update), the triangular inverse, and GPTQ's lazy batch update
+// W[:, later] -= Err @ U[block, later] ("Same Ruler, Smarter Placement: GPTQ", 1.8).
+// Products and sums are fp32, as the quantizer's arithmetic requires; the operands are
+// never rounded to a 16-bit type.
+//
+// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 MFMA blocks of 32 x 32).
+// Operands are staged k-major in LDS so that lanes 0..31 of an MFMA operand read 32
+// consecutive floats.  Triangular operands shrink the K range per tile; a lower-only
+// output skips tiles above the diagonal.
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int GT = 128;
+constexpr int GK = 16;
+constexpr int GP = GT + 4;  // LDS row length
+
+template <bool kTransB>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  const int n0 = blockIdx.x * GT, m0 = blockIdx.y * GT;
+  if ((g.flags & kLowerOut) && n0 > m0) return;
+  const int z = blockIdx.z;
+  const float* A = g.A + static_cast<int64_t>(z) * g.sA;
+  const float* B = g.B + static_cast<int64_t>(z) * g.sB;
+  float* C = g.C + static_cast<int64_t>(z) * g.sC;
+
+  int kb = 0, ke = g.K;
+  if (g.flags & kALower) ke = min(ke, m0 + GT);
+  if (g.flags & kBtLower) ke = min(ke, n0 + GT);
+  if (g.flags & kBLower) kb = max(kb, n0);
+  kb = kb / GK * GK;
+
+  __shared__ __attribute__((aligned(16))) float sA[2][GK][GP];
+  __shared__ __attribute__((aligned(16))) float sB[2][GK][GP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  float4 ra[2], rb[2];
+  // A tile [128 rows][16 k]: thread loads rows (tid>>2) and (tid>>2)+64, k = 4*(tid&3)..+3
+  auto load_rows = [&](const float* P, int64_t ld, int r0, int rlim, int k0, float4* r) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = r0 + (tid >> 2) + 64 * q;
+      const int k = k0 + 4 * (tid & 3);
+      if (row < rlim && k < ke) {
+        r[q] = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(row) * ld + k);
+        if (k + 4 > ke) {  // partial K vector: zero the tail
+          if (k + 1 >= ke) r[q].y = 0.0f;
+          if (k + 2 >= ke) r[q].z = 0.0f;
+          if (k + 3 >= ke) r[q].w = 0.0f;
+        }
+      } else {
+        r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  auto store_rows = [&](float (*s)[GP], const float4* r) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = (tid >> 2) + 64 * q;
+      const int k = 4 * (tid & 3);
+      s[k + 0][row] = r[q].x;
+      s[k + 1][row] = r[q].y;
+      s[k + 2][row] = r[q].z;
+      s[k + 3][row] = r[q].w;
+    }
+  };
+  // B tile [16 k][128 n] (no transpose): thread loads k = (tid>>5) and +8, n = 4*(tid&31)..+3
+  auto load_kmajor = [&](int k0, float4* r) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = k0 + (tid >> 5) + 8 * q;
+      const int n = n0 + 4 * (tid & 31);
+      if (k < ke && n < g.N) {
+        if (n + 4 <= g.N) {
+          r[q] = *reinterpret_cast<const float4*>(B + static_cast<int64_t>(k) * g.ldb + n);
+        } else {
+          const float* p = B + static_cast<int64_t>(k) * g.ldb + n;
+          r[q].x = p[0];
+          r[q].y = (n + 1 < g.N) ? p[1] : 0.0f;
+          r[q].z = (n + 2 < g.N) ? p[2] : 0.0f;
+          r[q].w = 0.0f;
+        }
+      } else {
+        r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  auto store_kmajor = [&](float (*s)[GP], const float4* r) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = (tid >> 5) + 8 * q;
+      *reinterpret_cast<float4*>(&s[k][4 * (tid & 31)]) = r[q];
+    }
+  };
+  auto load_b = [&](int k0) {
+    if constexpr (kTransB) load_rows(B, g.ldb, n0, g.N, k0, rb);
+    else load_kmajor(k0, rb);
+  };
+  auto store_b = [&](float (*s)[GP]) {
+    if constexpr (kTransB) store_rows(s, rb);
+    else store_kmajor(s, rb);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  const int nk = ke > kb ? (ke - kb + GK - 1) / GK : 0;
+  if (nk > 0) {
+    load_rows(A, g.lda, m0, g.M, kb, ra);
+    load_b(kb);
+    store_rows(sA[0], ra);
+    store_b(sB[0]);
+  }
+  __syncthreads();
+  const int l32 = lane & 31, kh = lane >> 5;
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nk;
+    if (more) {
+      load_rows(A, g.lda, m0, g.M, kb + (s + 1) * GK, ra);
+      load_b(kb + (s + 1) * GK);
+    }
+#pragma unroll
+    for (int kk = 0; kk < GK / 2; ++kk) {
+      float av[2], bv[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        av[b] = sA[buf][2 * kk + kh][64 * wm + 32 * b + l32];
+        bv[b] = sB[buf][2 * kk + kh][64 * wn + 32 * b + l32];
+      }
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[bm], bv[bn], acc[bm][bn], 0, 0, 0);
+    }
+    if (more) {
+      store_rows(sA[buf ^ 1], ra);
+      store_b(sB[buf ^ 1]);
+    }
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const int n = n0 + 64 * wn + 32 * bn + l32;
+        if (m < g.M && n < g.N) {
+          float* c = C + static_cast<int64_t>(m) * g.ldc + n;
+          const float v = g.alpha * acc[bm][bn][r];
+          *c = (g.beta != 0.0f) ? fmaf(g.beta, *c, v) : v;
+        }
+      }
+}
+
+}  // namespace
+
+gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return GPTQ_OK;
+  const dim3 grid((g.N + GT - 1) / GT, (g.M + GT - 1) / GT, g.batch);
+  if (g.transB) {
+    GPTQ_LAUNCH(gemm_f32_kernel<true>, grid, dim3(256), 0, stream, g);
+  } else {
+    GPTQ_LAUNCH(gemm_f32_kernel<false>, grid, dim3(256), 0, stream, g);
+  }
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

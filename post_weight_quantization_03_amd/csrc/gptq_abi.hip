@@ -1,0 +1,135 @@
+// C ABI of libgptq: argument validation and dispatch to the kernel enqueuers.
+// Every function declared in include/gptq.h is defined here.
+#include <cmath>
+
+#include "common.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_bytes(gptq_dtype t) { return t == GPTQ_F32 ? 4 : 2; }
+
+bool valid_dtype(int t) { return t == GPTQ_F32 || t == GPTQ_BF16 || t == GPTQ_F16; }
+
+// Quantizer parameters accepted by prepare/quantize.
+gptq_status check_params(const gptq_params* p, int d_in, bool need_grid) {
+  if (p == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (!(p->damp >= 0.0f) || !std::isfinite(p->damp)) return GPTQ_ERR_INVALID_ARG;
+  if (!need_grid) return GPTQ_OK;
+  if (p->bits < 2 || p->bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (p->block_size != gptq::kBlock) return GPTQ_ERR_INVALID_ARG;
+  const int g = p->group_size;
+  if (g != -1) {
+    if (g < 1 || gptq::kBlock % g != 0 || d_in % g != 0) return GPTQ_ERR_INVALID_ARG;
+    if (g != 16 && g != 32 && g != 64 && g != 128) return GPTQ_ERR_UNSUPPORTED;
+  }
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gptq_status gptq_accumulate_hessian(int batch, int d_in, int64_t n_tokens, gptq_dtype x_dtype, const void* X,
+                                    int64_t ldx, int64_t batch_stride_x, float* H, int64_t batch_stride_h,
+                                    double* diag_key, int64_t* n_seen, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  if (batch < 1 || d_in < 8 || d_in % 8 != 0 || n_tokens < 0 || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+  if (H == nullptr || diag_key == nullptr || n_seen == nullptr) return GPTQ_ERR_INVALID_ARG;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  if (batch_stride_h < dd && batch > 1) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(H, 16) || (batch > 1 && batch_stride_h % 4 != 0)) return GPTQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return GPTQ_OK;
+  const int64_t vec = 16 / static_cast<int64_t>(dtype_bytes(x_dtype));
+  if (X == nullptr || ldx < d_in || ldx % vec != 0 || !aligned(X, 16)) return GPTQ_ERR_INVALID_ARG;
+  if (batch > 1 && (batch_stride_x < ldx * n_tokens || batch_stride_x % vec != 0)) return GPTQ_ERR_INVALID_ARG;
+  return gptq::hessian_enqueue(batch, d_in, n_tokens, x_dtype, X, ldx, batch_stride_x, H,
+                               batch > 1 ? batch_stride_h : dd, diag_key, n_seen, workspace, workspace_bytes,
+                               stream);
+}
+
+gptq_status gptq_prepare_hinv(int batch, int d_in, const float* H, int64_t batch_stride_h, const double* diag_key,
+                              const gptq_params* p, float* U, int64_t batch_stride_u, int32_t* perm, uint8_t* dead,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 1 || d_in < gptq::kBlock || d_in % gptq::kBlock != 0) return GPTQ_ERR_INVALID_ARG;
+  if (H == nullptr || diag_key == nullptr || U == nullptr || perm == nullptr || dead == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  const gptq_status ps = check_params(p, d_in, false);
+  if (ps != GPTQ_OK) return ps;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  if (batch > 1 && (batch_stride_h < dd || batch_stride_u < dd || batch_stride_u % 4 != 0))
+    return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(U, 16)) return GPTQ_ERR_INVALID_ARG;
+  int not_spd = 0;
+  const gptq_status st = gptq::prepare_enqueue(batch, d_in, H, batch > 1 ? batch_stride_h : dd, diag_key, *p, U,
+                                               batch > 1 ? batch_stride_u : dd, perm, dead, workspace,
+                                               workspace_bytes, stream, &not_spd);
+  if (st != GPTQ_OK) return st;
+  return not_spd ? GPTQ_ERR_NOT_SPD : GPTQ_OK;
+}
+
+gptq_status gptq_quantize_layer(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
+                                int64_t batch_stride_w, const float* U, int64_t batch_stride_u, const int32_t* perm,
+                                const uint8_t* dead, const gptq_params* p, uint8_t* codes, float* scales,
+                                uint8_t* zeros, int32_t* g_idx, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (batch < 1 || d_out < 1 || d_in < gptq::kBlock || d_in % gptq::kBlock != 0 || !valid_dtype(w_dtype))
+    return GPTQ_ERR_INVALID_ARG;
+  if (W == nullptr || U == nullptr || perm == nullptr || dead == nullptr || codes == nullptr || scales == nullptr ||
+      zeros == nullptr || g_idx == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  const gptq_status ps = check_params(p, d_in, true);
+  if (ps != GPTQ_OK) return ps;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  if (ldw < d_in) return GPTQ_ERR_INVALID_ARG;
+  if (batch > 1 && (batch_stride_w < ldw * d_out || batch_stride_u < dd || batch_stride_u % 4 != 0))
+    return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(U, 16)) return GPTQ_ERR_INVALID_ARG;
+  return gptq::quantize_enqueue(batch, d_out, d_in, w_dtype, W, ldw, batch > 1 ? batch_stride_w : ldw * d_out, U,
+                                batch > 1 ? batch_stride_u : dd, perm, dead, *p, codes, scales, zeros, g_idx,
+                                workspace, workspace_bytes, stream);
+}
+
+gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const uint8_t* codes, const float* scales,
+                           const uint8_t* zeros, int32_t* qweight, int32_t* qzeros, uint16_t* scales_f16,
+                           hipStream_t stream) {
+  if (batch < 1 || d_out < 8 || d_out % 8 != 0 || d_in < 8 || d_in % 8 != 0 || n_groups < 1)
+    return GPTQ_ERR_INVALID_ARG;
+  if (codes == nullptr || scales == nullptr || zeros == nullptr || qweight == nullptr || qzeros == nullptr ||
+      scales_f16 == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  return gptq::pack_enqueue(batch, d_out, d_in, n_groups, codes, scales, zeros, qweight, qzeros, scales_f16, stream);
+}
+
+size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in, int64_t n_tokens_hint,
+                           const gptq_params* p) {
+  switch (which) {
+    case GPTQ_WS_HESSIAN:
+      if (d_in % 8 != 0) return 0;
+      return gptq::hessian_workspace(batch, d_in, n_tokens_hint);
+    case GPTQ_WS_PREPARE:
+      return gptq::prepare_workspace(batch, d_in);
+    case GPTQ_WS_QUANTIZE: {
+      if (p == nullptr) return 0;
+      return gptq::quantize_workspace(batch, d_out, d_in, *p);
+    }
+  }
+  return 0;
+}
+
+const char* gptq_status_string(gptq_status s) {
+  switch (s) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+    case GPTQ_ERR_NOT_SPD: return "damped Hessian is not positive definite";
+    case GPTQ_ERR_HIP: return "HIP runtime error";
+    case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case GPTQ_ERR_UNSUPPORTED: return "unsupported parameters";
+  }
+  return "unknown status";
+}
+
+const char* gptq_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header declares,
+sizes workspaces, and rejects bad arguments before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from post_weight_quantization_03_amd import gptq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:gptq_status|size_t|const char\*)\s+(gptq_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = gptq.lib()
+    names = declared_symbols()
+    assert names == set(gptq.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.gptq_version().decode().count(".") == 2
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert gptq.status_string(s)
+    assert "positive definite" in gptq.status_string(gptq.GPTQ_ERR_NOT_SPD)
+
+
+def test_workspace_sizes_are_positive_and_monotone():
+    p = gptq.Params(bits=4, group_size=128, act_order=True)
+    for d in (128, 256, 4096):
+        a = gptq.workspace_size(gptq.WS_PREPARE, 1, 0, d, 0, p)
+        b = gptq.workspace_size(gptq.WS_PREPARE, 2, 0, d, 0, p)
+        assert 0 < a < b
+        q1 = gptq.workspace_size(gptq.WS_QUANTIZE, 1, 64, d, 0, p)
+        q2 = gptq.workspace_size(gptq.WS_QUANTIZE, 1, 128, d, 0, p)
+        assert 0 < q1 < q2
+    h = [gptq.workspace_size(gptq.WS_HESSIAN, 1, 0, 4096, n, p) for n in (1, 2048, 65536, 131072, 1 << 20)]
+    assert all(x > 0 for x in h) and h == sorted(h)
+    assert gptq.workspace_size(gptq.WS_PREPARE, 1, 0, 100, 0, p) == 0   # d_in not a multiple of 128
+    assert gptq.workspace_size(gptq.WS_HESSIAN, 1, 0, 12, 10, p) == 0  # d_in not a multiple of 8
+
+
+def test_invalid_arguments_are_rejected_before_any_launch():
+    L = gptq.lib()
+    p = gptq.Params().c()
+    bad = gptq.GPTQ_ERR_INVALID_ARG
+    null = None
+    # batch 0, d_in not a multiple of 8, unknown dtype
+    assert L.gptq_accumulate_hessian(0, 128, 10, 1, 8, 128, 0, 16, 0, 8, 8, null, 0, null) == bad
+    assert L.gptq_accumulate_hessian(1, 12, 10, 1, 16, 16, 0, 16, 0, 8, 8, null, 0, null) == bad
+    assert L.gptq_accumulate_hessian(1, 128, 10, 7, 16, 128, 0, 16, 0, 8, 8, null, 0, null) == bad
+    # misaligned X pointer, row stride below d_in
+    assert L.gptq_accumulate_hessian(1, 128, 10, 1, 18, 128, 0, 16, 0, 8, 8, null, 0, null) == bad
+    assert L.gptq_accumulate_hessian(1, 128, 10, 1, 16, 64, 0, 16, 0, 8, 8, null, 0, null) == bad
+    # n_tokens == 0 is a no-op that needs no X
+    assert L.gptq_accumulate_hessian(1, 128, 0, 1, null, 128, 0, 16, 0, 8, 8, null, 0, null) == gptq.GPTQ_OK
+    # prepare: d_in not a multiple of 128, null params, negative damp
+    assert L.gptq_prepare_hinv(1, 100, 16, 0, 8, ctypes.byref(p), 16, 0, 8, 8, null, 0, null) == bad
+    assert L.gptq_prepare_hinv(1, 128, 16, 0, 8, None, 16, 0, 8, 8, null, 0, null) == bad
+    neg = gptq.Params(damp=-1.0).c()
+    assert L.gptq_prepare_hinv(1, 128, 16, 0, 8, ctypes.byref(neg), 16, 0, 8, 8, null, 0, null) == bad
+    # quantize: bits, block size, group size
+    for kw, code in [(dict(bits=1), bad), (dict(bits=9), bad), (dict(block_size=64), bad),
+                     (dict(group_size=48), bad), (dict(group_size=256), bad),
+                     (dict(group_size=8), gptq.GPTQ_ERR_UNSUPPORTED)]:
+        q = gptq.Params(**kw).c()
+        assert L.gptq_quantize_layer(1, 8, 128, 1, 16, 128, 0, 16, 0, 8, 8, ctypes.byref(q), 8, 8, 8, 8,
+                                     null, 0, null) == code, kw
+    # pack: d_out not a multiple of 8
+    assert L.gptq_pack_int4(1, 12, 128, 1, 8, 8, 8, 8, 8, 8, null) == bad
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gptq, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gptq, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        gptq.lib()

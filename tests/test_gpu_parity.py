@@ -1,0 +1,126 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle (MI355X only).
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still see several
+tiles and ragged tails (d_out not a multiple of 64, token counts not a multiple of the
+32-token stage, d_in not a multiple of the 256-wide Hessian tile).  Acceptance rules are
+in tests/parity.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import gptq_ref as R
+from post_weight_quantization_03_amd import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(what):
+    print(f"\n[gpu-case] {what}", flush=True)
+    sys.stdout.flush()
+
+
+CASES = {
+    # the tiny recipe at its full size: fp32 inputs, one grid per row, natural order
+    "tiny_full": synth.config("tiny"),
+    "attn_scaled": synth.scaled("attn_proj", d_out=200, d_in=512, n_tokens=5000, seq_len=1024),
+    "mlp_up_scaled": synth.scaled("mlp_up", d_out=328, d_in=384, n_tokens=4096, seq_len=1024),
+    "mlp_down_scaled": synth.scaled("mlp_down", d_out=128, d_in=640, n_tokens=3000, seq_len=1024),
+    "moe_scaled_4bit": synth.scaled("moe", d_out=96, d_in=256, n_tokens=1100, batch=4, seq_len=512),
+    "moe_scaled_3bit": synth.scaled("moe", d_out=96, d_in=256, n_tokens=1100, batch=4, seq_len=512, bits=3),
+    "group32_bf16": synth.scaled("attn_proj", d_out=72, d_in=256, n_tokens=2000, seq_len=1000, group_size=32),
+    "group64_f32": synth.scaled("attn_proj", d_out=40, d_in=384, n_tokens=1500, seq_len=500, group_size=64,
+                                dtype="f32"),
+    "group16_actorder": synth.scaled("attn_proj", d_out=33, d_in=256, n_tokens=900, seq_len=300, group_size=16),
+    "per_row_bf16_actorder": synth.scaled("mlp_up", d_out=64, d_in=256, n_tokens=700, seq_len=700, group_size=-1,
+                                          act_order=True),
+    "two_bit": synth.scaled("mlp_down", d_out=64, d_in=256, n_tokens=800, seq_len=800, bits=2),
+    "eight_bit": synth.scaled("attn_proj", d_out=64, d_in=256, n_tokens=800, seq_len=800, bits=8),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_parity(name):
+    spec = CASES[name]
+    announce(f"{name} {spec}")
+    Ws, Xs = parity.make_inputs(spec)
+    g = parity.run_gpu(spec, Ws, Xs)
+    for e in range(spec.batch):
+        rep = parity.check_problem(spec, Ws[e], Xs[e], g, e)
+        print(name, e, {k: (round(v, 9) if isinstance(v, float) else v) for k, v in rep.items()}, flush=True)
+
+
+def test_chunked_accumulation_and_empty_chunk():
+    spec = synth.scaled("attn_proj", d_out=64, d_in=256, n_tokens=3000, seq_len=1000)
+    announce("chunked accumulation 3000 tokens in 7 chunks")
+    import torch
+    from post_weight_quantization_03_amd import gptq
+    Ws, Xs = parity.make_inputs(spec)
+    X = parity.to_torch(Xs[0], "bf16")
+    H, key, n = gptq.new_hessian(256)
+    for a, b in [(0, 1), (1, 33), (33, 100), (100, 100), (100, 2047), (2047, 2999), (2999, 3000)]:
+        gptq.accumulate_hessian(X[a:b], H, key, n)
+    torch.cuda.synchronize()
+    Href, _ = R.ref_accumulate_hessian(Xs[0], "bf16")
+    Hg = H.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(Hg - Href) / np.linalg.norm(Href) <= parity.TOL_H
+    assert np.array_equal(Hg, Hg.T)
+    assert int(n.item()) == 3000
+    np.testing.assert_allclose(key.cpu().numpy(), np.diag(Href), rtol=parity.TOL_KEY)
+
+
+def test_dead_inputs():
+    spec = synth.scaled("attn_proj", d_out=48, d_in=256, n_tokens=1000, seq_len=1000)
+    announce("dead inputs")
+    Ws, Xs = parity.make_inputs(spec)
+    X = Xs[0].copy()
+    X[:, [0, 5, 130, 255]] = 0           # four inputs never active
+    g = parity.run_gpu(spec, Ws, [X])
+    assert g["dead"][0].nonzero()[0].tolist() == [0, 5, 130, 255]
+    parity.check_problem(spec, Ws[0], X, g, 0)
+
+
+def test_not_spd_is_reported():
+    announce("not SPD: damp 0, fewer tokens than inputs")
+    import torch
+    from post_weight_quantization_03_amd import gptq
+    spec = synth.scaled("attn_proj", d_out=8, d_in=256, n_tokens=64, seq_len=64)
+    Ws, Xs = parity.make_inputs(spec)
+    H, key, n = gptq.new_hessian(256)
+    gptq.accumulate_hessian(parity.to_torch(Xs[0], "bf16"), H, key, n)
+    with pytest.raises(R.NotSPD):
+        R.ref_prepare_hinv(R.ref_accumulate_hessian(Xs[0], "bf16")[0], 0.0, True)
+    with pytest.raises(gptq.NotSPDError):
+        gptq.prepare_hinv(H, key, gptq.Params(damp=0.0, act_order=True))
+    torch.cuda.synchronize()
+
+
+def test_pack_matches_oracle_bit_exactly():
+    announce("pack on seeded codes")
+    import torch
+    from post_weight_quantization_03_amd import gptq
+    rng = np.random.default_rng(123)
+    for batch, d_out, d_in, ng in [(1, 64, 256, 2), (3, 40, 384, 3), (1, 4096, 512, 4), (2, 8, 8, 1)]:
+        codes = rng.integers(0, 16, size=(batch, d_out, d_in)).astype(np.uint8)
+        zeros = rng.integers(0, 16, size=(batch, ng, d_out)).astype(np.uint8)
+        scales = (rng.random((batch, ng, d_out)) * 0.01).astype(np.float32)
+        qw, qz, sf = gptq.pack_int4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                                    torch.from_numpy(zeros).cuda())
+        torch.cuda.synchronize()
+        for e in range(batch):
+            rq, rz, rs = R.ref_pack_int4(codes[e], scales[e], zeros[e])
+            assert np.array_equal(qw[e].cpu().numpy(), rq)
+            assert np.array_equal(qz[e].cpu().numpy(), rz)
+            assert np.array_equal(sf[e].cpu().numpy().view(np.uint16), rs.view(np.uint16))
+
+
+def test_deterministic_repeat():
+    spec = synth.scaled("attn_proj", d_out=128, d_in=512, n_tokens=4096, seq_len=1024)
+    announce("determinism")
+    Ws, Xs = parity.make_inputs(spec)
+    a = parity.run_gpu(spec, Ws, Xs)
+    b = parity.run_gpu(spec, Ws, Xs)
+    for k in ("H", "diag_key", "U", "perm", "codes", "scales", "zeros", "g_idx"):
+        assert np.array_equal(a[k], b[k]), k
