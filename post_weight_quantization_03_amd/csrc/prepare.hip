@@ -31,8 +31,10 @@ constexpr int NB = 128;   // panel width (must equal the GEMM tile)
 constexpr int LP = NB + 1;
 
 // key[c] = diag_key[c], or 1 for a dead input; dead[c] = (diag_key[c] == 0).
+// Also clears the rank counters of actorder_rank_kernel.
 __global__ __launch_bounds__(256) void keys_kernel(const double* __restrict__ diag_key, int d_in,
-                                                   double* __restrict__ key, uint8_t* __restrict__ dead) {
+                                                   double* __restrict__ key, uint8_t* __restrict__ dead,
+                                                   int32_t* __restrict__ rank) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   const int e = blockIdx.y;
   if (c >= d_in) return;
@@ -40,32 +42,46 @@ __global__ __launch_bounds__(256) void keys_kernel(const double* __restrict__ di
   const double v = diag_key[o];
   key[o] = (v == 0.0) ? 1.0 : v;
   dead[o] = (v == 0.0) ? 1 : 0;
+  rank[o] = 0;
 }
 
-// perm[rank(c)] = c, rank(c) = #{j: key_j > key_c} + #{j < c: key_j == key_c}.
+// rank(c) = #{j: key_j > key_c} + #{j < c: key_j == key_c}, the position of c in a stable
+// descending sort.  Block (x, y): 256 candidates c against a slice of RANK_SLICE keys j;
+// the integer partial counts are summed with atomics (order-independent, exact).
+constexpr int RANK_SLICE = 512;
 __global__ __launch_bounds__(256) void actorder_rank_kernel(const double* __restrict__ key, int d_in,
-                                                            int act_order, int32_t* __restrict__ perm) {
-  __shared__ double sk[256];
+                                                            int32_t* __restrict__ rank) {
+  __shared__ double sk[RANK_SLICE];
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int j0 = blockIdx.y * RANK_SLICE;
+  const int e = blockIdx.z;
+  const double* k = key + static_cast<int64_t>(e) * d_in;
+  for (int i = threadIdx.x; i < RANK_SLICE; i += 256) sk[i] = (j0 + i < d_in) ? k[j0 + i] : 0.0;
+  __syncthreads();
+  if (c >= d_in) return;
+  const double kc = k[c];
+  const int jn = min(RANK_SLICE, d_in - j0);
+  int cnt = 0;
+  for (int j = 0; j < jn; ++j) {
+    const double kj = sk[j];
+    cnt += (kj > kc) || (kj == kc && j0 + j < c);
+  }
+  if (cnt) atomicAdd(rank + static_cast<int64_t>(e) * d_in + c, cnt);
+}
+
+// perm[rank(c)] = c (ActOrder), or the identity.
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ rank, int d_in,
+                                                           int act_order, int32_t* __restrict__ perm) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   const int e = blockIdx.y;
-  const double* k = key + static_cast<int64_t>(e) * d_in;
+  if (c >= d_in) return;
+  const int64_t o = static_cast<int64_t>(e) * d_in;
   if (!act_order) {
-    if (c < d_in) perm[static_cast<int64_t>(e) * d_in + c] = c;
+    perm[o + c] = c;
     return;
   }
-  const double kc = (c < d_in) ? k[c] : 0.0;
-  int rank = 0;
-  for (int j0 = 0; j0 < d_in; j0 += 256) {
-    __syncthreads();
-    sk[threadIdx.x] = (j0 + threadIdx.x < d_in) ? k[j0 + threadIdx.x] : 0.0;
-    __syncthreads();
-    const int jn = min(256, d_in - j0);
-    for (int j = 0; j < jn; ++j) {
-      const double kj = sk[j];
-      rank += (kj > kc) || (kj == kc && j0 + j < c);
-    }
-  }
-  if (c < d_in) perm[static_cast<int64_t>(e) * d_in + rank] = c;
+  const int r = min(max(rank[o + c], 0), d_in - 1);
+  perm[o + r] = c;
 }
 
 // lambda[e] = damp * mean(key[e]) (fixed-order tree sum in fp64).
@@ -112,74 +128,150 @@ __global__ __launch_bounds__(256) void gather_reversed_kernel(const float* __res
   A[(static_cast<int64_t>(e) * d_in + r) * d_in + c] = v;
 }
 
-// Factor the diagonal block k of A (lower part) in LDS: writes L_kk into Lbuf and
-// L_kk^-1 into Linv (both full 128x128 blocks, zeros above the diagonal).
+// Factor the diagonal block k of A (lower part): writes L_kk into Lbuf and L_kk^-1 into
+// Linv (both full 128x128 blocks, zeros above the diagonal).
+//
+// Each of the 256 threads keeps an 8x8 sub-block of the 128x128 block in registers
+// (thread t: block row t/16, block column t%16; a wave covers 32 consecutive rows).
+// Cholesky, right-looking on unscaled columns: at step j every element with
+// j < c, j < i takes a_ic -= a_ij a_cj / a_jj; column j (zeros at rows <= j) and the pivot
+// a_jj are broadcast through LDS by the threads that own them, so each step costs one
+// barrier.  Afterwards l_ij = a_ij / sqrt(a_jj).  The inverse X = L^-1 is then formed the
+// same way, row by row: row k of X is final once divided by l_kk, and every row i > k
+// subtracts l_ik times it.  Loops over columns are unrolled by 8 so that register
+// indices stay compile-time constants.
 __global__ __launch_bounds__(256) void potrf_block_kernel(const float* __restrict__ A, float* __restrict__ Lbuf,
                                                           int64_t bsl, float* __restrict__ Linv, int d_in,
                                                           int k0, int* __restrict__ flag) {
-  __shared__ float sa[NB][LP];
-  __shared__ float sx[NB][LP];
+  __shared__ float sL[NB][LP];
+  __shared__ float colbuf[2][NB];
+  __shared__ float piv[NB];
   const int e = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float* Ae = A + static_cast<int64_t>(e) * d_in * d_in;
-  for (int i = tid; i < NB * NB; i += 256) {
-    const int r = i / NB, c = i % NB;
-    sa[r][c] = (c <= r) ? Ae[static_cast<int64_t>(k0 + r) * d_in + k0 + c] : 0.0f;
+  const int t = threadIdx.x;
+  const int br = t >> 4, bc = t & 15;
+  const int r0 = 8 * br, c0 = 8 * bc;
+  const int wave_last_row = 32 * (t >> 6) + 31;
+  const float* Ae = A + static_cast<int64_t>(e) * d_in * d_in + static_cast<int64_t>(k0) * d_in + k0;
+
+  float a[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float4* src = reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(r0 + r) * d_in + c0);
+    const float4 u = src[0], v = src[1];
+    a[r][0] = u.x; a[r][1] = u.y; a[r][2] = u.z; a[r][3] = u.w;
+    a[r][4] = v.x; a[r][5] = v.y; a[r][6] = v.z; a[r][7] = v.w;
+  }
+  // publish column 0
+  if (bc == 0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) colbuf[0][r0 + r] = (r0 + r > 0) ? a[r][0] : 0.0f;
+    if (br == 0) piv[0] = a[0][0];
   }
   __syncthreads();
-  // Right-looking elimination on unscaled columns: at step j, a_ic -= a_ij a_cj / a_jj for
-  // j < c <= i.  Afterwards l_ij = a_ij / sqrt(a_jj).
-  bool bad = false;
-  for (int j = 0; j < NB; ++j) {
-    const float piv = sa[j][j];
-    if (!(piv > 0.0f) || !isfinite(piv)) bad = true;
-    const float rp = 1.0f / piv;
-    const int m = NB - 1 - j;                 // trailing size
-    const int cnt = m * (m + 1) / 2;
-    for (int t = tid; t < cnt; t += 256) {
-      // t -> (i, c) with j < c <= i, enumerated row by row of the trailing triangle
-      int ii = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-      while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
-      while (ii * (ii + 1) / 2 > t) --ii;
-      const int cc = t - ii * (ii + 1) / 2;
-      const int i = j + 1 + ii, c = j + 1 + cc;
-      sa[i][c] = fmaf(-sa[i][j] * rp, sa[c][j], sa[i][c]);
+  for (int jb = 0; jb < NB / 8; ++jb) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = 8 * jb + jj;
+      const int buf = jj & 1;
+      if (wave_last_row > j) {
+        const float rp = 1.0f / piv[j];
+        float ci[8], cc[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) ci[r] = colbuf[buf][r0 + r] * rp;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) cc[c] = colbuf[buf][c0 + c];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) a[r][c] = fmaf(-ci[r], cc[c], a[r][c]);
+      }
+      // publish column j + 1 (its owners are block column (j+1)/8, local column (jj+1)%8)
+      const int jn = j + 1;
+      if (jn < NB && bc == (jn >> 3)) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) colbuf[buf ^ 1][r0 + r] = (r0 + r > jn) ? a[r][(jj + 1) & 7] : 0.0f;
+        if (br == bc) piv[jn] = a[(jj + 1) & 7][(jj + 1) & 7];
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
-  if (bad && tid == 0) flag[e] = 1;
-  // scale columns: l_ij = a_ij / sqrt(a_jj); the diagonal becomes sqrt(a_jj)
-  for (int i = tid; i < NB * NB; i += 256) {
-    const int r = i / NB, c = i % NB;
-    if (c < r) sa[r][c] = sa[r][c] / sqrtf(sa[c][c]);
+  // every pivot must be positive and finite
+  if (t == 0) {
+    bool bad = false;
+    for (int j = 0; j < NB; ++j) bad |= !(piv[j] > 0.0f) || !isfinite(piv[j]);
+    if (bad) flag[e] = 1;
   }
-  __syncthreads();
-  for (int r = tid; r < NB; r += 256) sa[r][r] = sqrtf(sa[r][r]);
-  __syncthreads();
-  // X = L^-1 by elimination on the identity: at step k every row i > k subtracts
-  // (l_ik / l_kk) times the (still unscaled) row k; finally row k is divided by l_kk.
-  for (int i = tid; i < NB * NB; i += 256) sx[i / NB][i % NB] = (i / NB == i % NB) ? 1.0f : 0.0f;
-  __syncthreads();
-  for (int k = 0; k < NB - 1; ++k) {
-    const float rk = 1.0f / sa[k][k];
-    const int rows = NB - 1 - k, cols = k + 1;
-    for (int t = tid; t < rows * cols; t += 256) {
-      const int i = k + 1 + t / cols, c = t % cols;
-      sx[i][c] = fmaf(-sa[i][k] * rk, sx[k][c], sx[i][c]);
+  // scale: l_ic = a_ic / sqrt(a_cc), l_cc = sqrt(a_cc)
+  float sq[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sq[c] = sqrtf(piv[c0 + c]);
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int i = r0 + r, cg = c0 + c;
+      const float v = (i > cg) ? a[r][c] / sq[c] : (i == cg ? sq[c] : 0.0f);
+      a[r][c] = v;
+      sL[i][cg] = v;
     }
-    __syncthreads();
+  float* Le = Lbuf + static_cast<int64_t>(e) * bsl + static_cast<int64_t>(k0) * d_in + k0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float4* dst = reinterpret_cast<float4*>(Le + static_cast<int64_t>(r0 + r) * d_in + c0);
+    dst[0] = make_float4(a[r][0], a[r][1], a[r][2], a[r][3]);
+    dst[1] = make_float4(a[r][4], a[r][5], a[r][6], a[r][7]);
   }
-  for (int i = tid; i < NB * NB; i += 256) {
-    const int r = i / NB, c = i % NB;
-    if (c <= r) sx[r][c] = sx[r][c] / sa[r][r];
+  // X = L^-1: start from the identity; row 0 of X is e_0 / l_00.
+  float x[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[r][c] = (r0 + r == c0 + c) ? 1.0f : 0.0f;
+  __syncthreads();   // sL complete
+  if (br == 0) {
+    const float inv0 = 1.0f / sL[0][0];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      x[0][c] *= inv0;
+      colbuf[0][c0 + c] = x[0][c];
+    }
   }
   __syncthreads();
-  float* Le = Lbuf + static_cast<int64_t>(e) * bsl;
-  float* Xe = Linv + static_cast<int64_t>(e) * d_in * d_in;
-  for (int i = tid; i < NB * NB; i += 256) {
-    const int r = i / NB, c = i % NB;
-    Le[static_cast<int64_t>(k0 + r) * d_in + k0 + c] = (c <= r) ? sa[r][c] : 0.0f;
-    Xe[static_cast<int64_t>(k0 + r) * d_in + k0 + c] = (c <= r) ? sx[r][c] : 0.0f;
+  for (int kb = 0; kb < NB / 8; ++kb) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int k = 8 * kb + kk;
+      const int buf = kk & 1;
+      if (wave_last_row > k) {
+        float m[8], xr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r] = (r0 + r > k) ? sL[r0 + r][k] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xr[c] = colbuf[buf][c0 + c];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) x[r][c] = fmaf(-m[r], xr[c], x[r][c]);
+      }
+      // row k + 1 is now final up to its diagonal scale: its owners scale and publish it
+      const int kn = k + 1;
+      if (kn < NB && br == (kn >> 3)) {
+        const float inv = 1.0f / sL[kn][kn];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          x[(kk + 1) & 7][c] *= inv;
+          colbuf[buf ^ 1][c0 + c] = x[(kk + 1) & 7][c];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  float* Xe = Linv + static_cast<int64_t>(e) * d_in * d_in + static_cast<int64_t>(k0) * d_in + k0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float4* dst = reinterpret_cast<float4*>(Xe + static_cast<int64_t>(r0 + r) * d_in + c0);
+    dst[0] = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
+    dst[1] = make_float4(x[r][4], x[r][5], x[r][6], x[r][7]);
   }
 }
 
@@ -197,6 +289,7 @@ __global__ __launch_bounds__(256) void reverse_to_upper_kernel(const float* __re
 
 struct PrepWs {
   double* key;
+  int32_t* rank;
   double* lambda;
   int* flag;
   float* A;
@@ -210,6 +303,7 @@ PrepWs carve(void* ws, int batch, int d_in) {
   PrepWs w{};
   const size_t dd = static_cast<size_t>(d_in) * d_in;
   w.key = cv.take<double>(static_cast<size_t>(batch) * d_in);
+  w.rank = cv.take<int32_t>(static_cast<size_t>(batch) * d_in);
   w.lambda = cv.take<double>(batch);
   w.flag = cv.take<int>(batch);
   w.A = cv.take<float>(batch * dd);
@@ -264,8 +358,12 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
   const dim3 blk(256);
   const int cb = (d_in + 255) / 256;
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
-  GPTQ_LAUNCH(keys_kernel, dim3(cb, batch), blk, 0, stream, diag_key, d_in, w.key, dead);
-  GPTQ_LAUNCH(actorder_rank_kernel, dim3(cb, batch), blk, 0, stream, w.key, d_in, p.act_order, perm);
+  GPTQ_LAUNCH(keys_kernel, dim3(cb, batch), blk, 0, stream, diag_key, d_in, w.key, dead, w.rank);
+  if (p.act_order) {
+    GPTQ_LAUNCH(actorder_rank_kernel, dim3(cb, (d_in + RANK_SLICE - 1) / RANK_SLICE, batch), blk, 0, stream, w.key,
+                d_in, w.rank);
+  }
+  GPTQ_LAUNCH(perm_scatter_kernel, dim3(cb, batch), blk, 0, stream, w.rank, d_in, p.act_order, perm);
   GPTQ_LAUNCH(damping_kernel, dim3(batch), blk, 0, stream, w.key, d_in, static_cast<double>(p.damp),
               w.lambda, w.flag);
   GPTQ_LAUNCH(gather_reversed_kernel, dim3(cb, d_in, batch), blk, 0, stream, H, bsh, perm, w.key,

@@ -111,7 +111,7 @@ def check_problem(spec, W, X, g: dict, e: int, rows: np.ndarray | None = None, r
     rep_ = R.ref_quantize_layer(Wr, spec.dtype, prep, spec.bits, spec.group_size, spec.block_size,
                                 forced_codes=codes_g, forced_zeros=zeros_g)
     grid = rep_["grid"]
-    divs = grid.code_div + [(r, c, gap, d) for (_, r, gap, d) in grid.zero_div]
+    divs = grid.code_div + [(r, gi, gap, d) for (gi, r, gap, d) in grid.zero_div]
     rep["n_entries"] = int(codes_g.size)
     rep["divergences"] = len(divs)
     rep["max_div_gap"] = max([dv[2] for dv in divs], default=0.0)
