@@ -7,7 +7,8 @@
 // Products and sums are fp32, as the quantizer's arithmetic requires; the operands are
 // never rounded to a 16-bit type.
 //
-// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 MFMA blocks of 32 x 32).
+// Tile 128 x 128 x 32 (or 64 x 64 x 32 when the grid would be small), 256 threads = 4
+// waves, each owning a quarter of the tile as 32 x 32 MFMA blocks.
 // Operands are staged k-major in LDS so that lanes 0..31 of an MFMA operand read 32
 // consecutive floats.  Triangular operands shrink the K range per tile; a lower-only
 // output skips tiles above the diagonal.
@@ -16,12 +17,16 @@
 namespace gptq {
 namespace {
 
-constexpr int GT = 128;
-constexpr int GK = 16;
-constexpr int GP = GT + 4;  // LDS row length
+constexpr int GK = 32;
 
-template <bool kTransB>
+// TT = output tile edge (128 or 64); each of the 4 waves owns a (TT/2) x (TT/2) quarter as
+// MB x MB blocks of 32 x 32.
+template <bool kTransB, int TT>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int GT = TT;
+  constexpr int GP = GT + 4;  // LDS row length
+  constexpr int MB = TT / 64;
+  constexpr int RQ = GT / 32;  // row-vector loads per thread (rows of 32 k)
   const int n0 = blockIdx.x * GT, m0 = blockIdx.y * GT;
   if ((g.flags & kLowerOut) && n0 > m0) return;
   const int z = blockIdx.z;
@@ -41,13 +46,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  float4 ra[2], rb[2];
-  // A tile [128 rows][16 k]: thread loads rows (tid>>2) and (tid>>2)+64, k = 4*(tid&3)..+3
+  float4 ra[RQ], rb[RQ];
+  // A tile [GT rows][32 k]: thread loads rows (tid>>3) + 32q, k = 4*(tid&7)..+3
   auto load_rows = [&](const float* P, int64_t ld, int r0, int rlim, int k0, float4* r) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = r0 + (tid >> 2) + 64 * q;
-      const int k = k0 + 4 * (tid & 3);
+    for (int q = 0; q < RQ; ++q) {
+      const int row = r0 + (tid >> 3) + 32 * q;
+      const int k = k0 + 4 * (tid & 7);
       if (row < rlim && k < ke) {
         r[q] = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(row) * ld + k);
         if (k + 4 > ke) {  // partial K vector: zero the tail
@@ -62,21 +67,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   };
   auto store_rows = [&](float (*s)[GP], const float4* r) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = (tid >> 2) + 64 * q;
-      const int k = 4 * (tid & 3);
+    for (int q = 0; q < RQ; ++q) {
+      const int row = (tid >> 3) + 32 * q;
+      const int k = 4 * (tid & 7);
       s[k + 0][row] = r[q].x;
       s[k + 1][row] = r[q].y;
       s[k + 2][row] = r[q].z;
       s[k + 3][row] = r[q].w;
     }
   };
-  // B tile [16 k][128 n] (no transpose): thread loads k = (tid>>5) and +8, n = 4*(tid&31)..+3
+  // B tile [32 k][GT n] (no transpose): thread loads k = tid / (GT/4) + (256*4/GT) q,
+  // n = 4 * (tid % (GT/4))
+  constexpr int NV = GT / 4;        // float4 per k row
+  constexpr int KS = 256 / NV;      // k rows covered by one pass of the block
   auto load_kmajor = [&](int k0, float4* r) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k = k0 + (tid >> 5) + 8 * q;
-      const int n = n0 + 4 * (tid & 31);
+    for (int q = 0; q < RQ; ++q) {
+      const int k = k0 + tid / NV + KS * q;
+      const int n = n0 + 4 * (tid % NV);
       if (k < ke && n < g.N) {
         if (n + 4 <= g.N) {
           r[q] = *reinterpret_cast<const float4*>(B + static_cast<int64_t>(k) * g.ldb + n);
@@ -94,9 +102,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   };
   auto store_kmajor = [&](float (*s)[GP], const float4* r) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k = (tid >> 5) + 8 * q;
-      *reinterpret_cast<float4*>(&s[k][4 * (tid & 31)]) = r[q];
+    for (int q = 0; q < RQ; ++q) {
+      const int k = tid / NV + KS * q;
+      *reinterpret_cast<float4*>(&s[k][4 * (tid % NV)]) = r[q];
     }
   };
   auto load_b = [&](int k0) {
@@ -108,11 +116,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     else store_kmajor(s, rb);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MB][MB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -134,16 +142,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int kk = 0; kk < GK / 2; ++kk) {
-      float av[2], bv[2];
+      float av[MB], bv[MB];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        av[b] = sA[buf][2 * kk + kh][64 * wm + 32 * b + l32];
-        bv[b] = sB[buf][2 * kk + kh][64 * wn + 32 * b + l32];
+      for (int b = 0; b < MB; ++b) {
+        av[b] = sA[buf][2 * kk + kh][(GT / 2) * wm + 32 * b + l32];
+        bv[b] = sB[buf][2 * kk + kh][(GT / 2) * wn + 32 * b + l32];
       }
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
+      for (int bm = 0; bm < MB; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
+        for (int bn = 0; bn < MB; ++bn)
           acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[bm], bv[bn], acc[bm][bn], 0, 0, 0);
     }
     if (more) {
@@ -155,13 +163,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
   // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
+  for (int bm = 0; bm < MB; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn)
+    for (int bn = 0; bn < MB; ++bn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const int n = n0 + 64 * wn + 32 * bn + l32;
+        const int m = m0 + (GT / 2) * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const int n = n0 + (GT / 2) * wn + 32 * bn + l32;
         if (m < g.M && n < g.N) {
           float* c = C + static_cast<int64_t>(m) * g.ldc + n;
           const float v = g.alpha * acc[bm][bn][r];
@@ -174,11 +182,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return GPTQ_OK;
-  const dim3 grid((g.N + GT - 1) / GT, (g.M + GT - 1) / GT, g.batch);
-  if (g.transB) {
-    GPTQ_LAUNCH(gemm_f32_kernel<true>, grid, dim3(256), 0, stream, g);
+  // 128-wide tiles when they alone give every CU at least two workgroups, else 64-wide
+  const int64_t tiles128 = static_cast<int64_t>((g.N + 127) / 128) * ((g.M + 127) / 128) * g.batch;
+  const bool big = tiles128 >= 512;
+  const int T = big ? 128 : 64;
+  const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, g.batch);
+  if (big) {
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 128>), grid, dim3(256), 0, stream, g);
   } else {
-    GPTQ_LAUNCH(gemm_f32_kernel<false>, grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64>), grid, dim3(256), 0, stream, g);
   }
   return GPTQ_OK;
 }

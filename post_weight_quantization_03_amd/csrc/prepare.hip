@@ -12,14 +12,10 @@
 //      positive-diagonal upper factor the pages obtain with chol / cholesky_inverse / chol,
 //      at 2/3 d^3 instead of 4/3 d^3 flops.
 //
-// Cholesky: right-looking with 128-column panels.  A single workgroup factors the
-// diagonal block in LDS and inverts it; the panel below is the product of the panel with
-// that inverse (transposed), and the trailing lower tiles take a symmetric rank-128
-// update — both on the fp32 matrix cores.  The inverse L^-1 is assembled bottom-up:
-// diagonal blocks come from the panel kernel, off-diagonal blocks from
-// inv([[L11, 0], [L21, L22]]) = [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]] over a
-// recursive split.  A non-positive or non-finite pivot sets a device flag that the host
-// reads back (GPTQ_ERR_NOT_SPD).
+// Cholesky and inverse together by recursive halving (chol_inv below): one workgroup
+// factors and inverts each 128-column diagonal block in registers/LDS; everything else is
+// fp32 matrix-core products.  A non-positive or non-finite pivot sets a device flag that
+// the host reads back (GPTQ_ERR_NOT_SPD).
 #include <algorithm>
 
 #include "common.h"
@@ -313,34 +309,56 @@ PrepWs carve(void* ws, int batch, int d_in) {
   return w;
 }
 
-// Off-diagonal blocks of L^-1 for the block range [b0, b1) (block = NB columns).
-gptq_status tri_inverse(int b0, int b1, int batch, int d_in, const float* L, int64_t bsl, float* Linv,
-                        float* T, hipStream_t stream) {
-  if (b1 - b0 <= 1) return GPTQ_OK;
-  const int bm = b0 + (b1 - b0) / 2;
-  gptq_status st = tri_inverse(b0, bm, batch, d_in, L, bsl, Linv, T, stream);
-  if (st != GPTQ_OK) return st;
-  st = tri_inverse(bm, b1, batch, d_in, L, bsl, Linv, T, stream);
-  if (st != GPTQ_OK) return st;
-  const int o1 = b0 * NB, o2 = bm * NB, h1 = (bm - b0) * NB, h2 = (b1 - bm) * NB;
+// Recursive Cholesky with the inverse, over the block range [b0, b1) of A (in place):
+//   [A11  .  ]   [L11  0 ]            L11, L11^-1 = recurse(A11)
+//   [A21 A22 ] = [L21 L22] [..]^T     L21 = A21 L11^-T           (product with L11^-1)
+//                                     S   = A22 - L21 L21^T      (lower tiles, in place)
+//                                     L22, L22^-1 = recurse(S)
+//   L^-1 = [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]].
+// Leaves are single 128-column blocks (potrf_block_kernel).  Every product runs on the
+// fp32 matrix cores with triangular operands trimming the K range; most of the flops land
+// in the large products near the top of the recursion.
+gptq_status chol_inv(int b0, int b1, int batch, int d_in, float* A, float* L, int64_t bsl, float* Linv, float* T,
+                     int* flag, hipStream_t stream) {
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
-  // T = L21 * L11^-1     (L11^-1 lower: K starts at the output column)
+  if (b1 - b0 == 1) {
+    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, stream, A, L, bsl, Linv, d_in, b0 * NB, flag);
+    return GPTQ_OK;
+  }
+  const int bm = b0 + (b1 - b0) / 2;
+  const int o1 = b0 * NB, o2 = bm * NB, h1 = (bm - b0) * NB, h2 = (b1 - bm) * NB;
+  gptq_status st = chol_inv(b0, bm, batch, d_in, A, L, bsl, Linv, T, flag, stream);
+  if (st != GPTQ_OK) return st;
   GemmArgs g{};
+  // L21 = A21 * (L11^-1)^T
+  g.M = h2; g.N = h1; g.K = h1;
+  g.A = A + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = dd;
+  g.B = Linv + static_cast<int64_t>(o1) * d_in + o1; g.ldb = d_in; g.sB = dd;
+  g.C = L + static_cast<int64_t>(o2) * d_in + o1; g.ldc = d_in; g.sC = bsl;
+  g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower; g.batch = batch;
+  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
+  // S = A22 - L21 L21^T (lower tiles)
+  g.M = h2; g.N = h2; g.K = h1;
+  g.A = L + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = bsl;
+  g.B = g.A; g.ldb = d_in; g.sB = bsl;
+  g.C = A + static_cast<int64_t>(o2) * d_in + o2; g.ldc = d_in; g.sC = dd;
+  g.alpha = -1.0f; g.beta = 1.0f; g.transB = 1; g.flags = kLowerOut;
+  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
+  if ((st = chol_inv(bm, b1, batch, d_in, A, L, bsl, Linv, T, flag, stream)) != GPTQ_OK) return st;
+  // T = L21 * L11^-1   (L11^-1 lower: the K range of an output column starts at it)
   g.M = h2; g.N = h1; g.K = h1;
   g.A = L + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = bsl;
   g.B = Linv + static_cast<int64_t>(o1) * d_in + o1; g.ldb = d_in; g.sB = dd;
   g.C = T; g.ldc = h1; g.sC = static_cast<int64_t>(h2) * h1;
-  g.alpha = 1.0f; g.beta = 0.0f; g.transB = 0; g.flags = kBLower; g.batch = batch;
-  st = gemm_f32(g, stream);
-  if (st != GPTQ_OK) return st;
-  // Linv21 = -L22^-1 * T   (L22^-1 lower: K ends at the output row)
-  GemmArgs h{};
-  h.M = h2; h.N = h1; h.K = h2;
-  h.A = Linv + static_cast<int64_t>(o2) * d_in + o2; h.lda = d_in; h.sA = dd;
-  h.B = T; h.ldb = h1; h.sB = static_cast<int64_t>(h2) * h1;
-  h.C = Linv + static_cast<int64_t>(o2) * d_in + o1; h.ldc = d_in; h.sC = dd;
-  h.alpha = -1.0f; h.beta = 0.0f; h.transB = 0; h.flags = kALower; h.batch = batch;
-  return gemm_f32(h, stream);
+  g.alpha = 1.0f; g.beta = 0.0f; g.transB = 0; g.flags = kBLower;
+  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
+  // Linv21 = -L22^-1 * T   (L22^-1 lower: the K range of an output row ends at it)
+  g.M = h2; g.N = h1; g.K = h2;
+  g.A = Linv + static_cast<int64_t>(o2) * d_in + o2; g.lda = d_in; g.sA = dd;
+  g.B = T; g.ldb = h1; g.sB = static_cast<int64_t>(h2) * h1;
+  g.C = Linv + static_cast<int64_t>(o2) * d_in + o1; g.ldc = d_in; g.sC = dd;
+  g.alpha = -1.0f; g.beta = 0.0f; g.transB = 0; g.flags = kALower;
+  return gemm_f32(g, stream);
 }
 
 }  // namespace
@@ -369,33 +387,7 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
   GPTQ_LAUNCH(gather_reversed_kernel, dim3(cb, d_in, batch), blk, 0, stream, H, bsh, perm, w.key,
               w.lambda, d_in, w.A);
   // L is built in the U buffer (same shape), then replaced by U at the end.
-  float* L = U;
-  const int nblk = d_in / NB;
-  for (int kb = 0; kb < nblk; ++kb) {
-    const int k0 = kb * NB;
-    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), blk, 0, stream, w.A, L, bsu, w.Linv, d_in, k0, w.flag);
-    const int rest = d_in - k0 - NB;
-    if (rest == 0) break;
-    // panel: L[k0+NB:, k-block] = A[k0+NB:, k-block] * (L_kk^-1)^T
-    GemmArgs g{};
-    g.M = rest; g.N = NB; g.K = NB;
-    g.A = w.A + static_cast<int64_t>(k0 + NB) * d_in + k0; g.lda = d_in; g.sA = dd;
-    g.B = w.Linv + static_cast<int64_t>(k0) * d_in + k0; g.ldb = d_in; g.sB = dd;
-    g.C = L + static_cast<int64_t>(k0 + NB) * d_in + k0; g.ldc = d_in; g.sC = bsu;
-    g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower; g.batch = batch;
-    gptq_status st = gemm_f32(g, stream);
-    if (st != GPTQ_OK) return st;
-    // trailing: A[k0+NB:, k0+NB:] -= P P^T (lower tiles)
-    GemmArgs h{};
-    h.M = rest; h.N = rest; h.K = NB;
-    h.A = L + static_cast<int64_t>(k0 + NB) * d_in + k0; h.lda = d_in; h.sA = bsu;
-    h.B = h.A; h.ldb = d_in; h.sB = bsu;
-    h.C = w.A + static_cast<int64_t>(k0 + NB) * d_in + k0 + NB; h.ldc = d_in; h.sC = dd;
-    h.alpha = -1.0f; h.beta = 1.0f; h.transB = 1; h.flags = kLowerOut; h.batch = batch;
-    st = gemm_f32(h, stream);
-    if (st != GPTQ_OK) return st;
-  }
-  gptq_status st = tri_inverse(0, nblk, batch, d_in, L, bsu, w.Linv, w.T, stream);
+  gptq_status st = chol_inv(0, d_in / NB, batch, d_in, w.A, U, bsu, w.Linv, w.T, w.flag, stream);
   if (st != GPTQ_OK) return st;
   GPTQ_LAUNCH(reverse_to_upper_kernel, dim3(cb, d_in, batch), blk, 0, stream, w.Linv, d_in, U, bsu);
 

@@ -15,8 +15,9 @@
 //                    every lane quantizes its own row, so the column recurrence needs no
 //                    cross-lane traffic.  U's diagonal block is wave-uniform and is read
 //                    through the scalar cache.  Outputs codes (processing order), the
-//                    group scale/zero, and Err [d_out, 128].
-//     lazy update:   W_p[:, j2:] -= Err @ U[b-block, j2:] on the fp32 matrix cores.
+//                    group scale/zero, and the block's columns of Err.
+//     lazy update:   hierarchical (see sweep_range): W_p[:, right] -= Err[:, left] @ U[left,
+//                    right] on the fp32 matrix cores, Err [d_out, d_in] in processing order.
 //   unpermute:       codes back to original column order; g_idx.
 #include "common.h"
 
@@ -141,9 +142,131 @@ __global__ __launch_bounds__(64) void block_sweep_kernel(const float* __restrict
   uint4* cdst = reinterpret_cast<uint4*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
 #pragma unroll
   for (int i = 0; i < kBlock / 16; ++i) cdst[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
-  float4* edst = reinterpret_cast<float4*>(err + (static_cast<int64_t>(e) * d_out + r) * kBlock);
+  float4* edst = reinterpret_cast<float4*>(err + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
 #pragma unroll
   for (int i = 0; i < kBlock / 4; ++i) edst[i] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+}
+
+// Broadcast lane `src` of each group of four lanes (DPP quad_perm).
+template <int src>
+__device__ __forceinline__ float quad_bcast(float v) {
+  constexpr int ctrl = src | (src << 2) | (src << 4) | (src << 6);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // [1,0,3,2]
+  return fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // [2,3,0,1]
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+}
+
+constexpr int QP = 36;   // LDS stride (floats) of one lane's 32 U values of a row
+
+// One 128-column block of the sweep with four lanes per row: lane k of a quad keeps
+// columns 4m + k (m = 0..31) of its row in registers.  For column j, the owner lane's
+// value is broadcast to the quad (DPP), every lane of the quad quantizes it (so all four
+// hold err_j and code_j), and each lane updates its own later columns.  The U block sits
+// in LDS as Ul[j][k][m] = U[j0 + j][j0 + 4m + k] with its diagonal zeroed (1/U_jj kept
+// apart), so a lane's update reads are contiguous and columns at or before j get a zero
+// factor.  A workgroup of 256 threads handles 64 rows.
+template <int G>
+__global__ __launch_bounds__(256) void block_sweep_quad_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
+                                                               int64_t bsu, int d_out, int d_in, int blk, float maxq,
+                                                               float* __restrict__ scales, uint8_t* __restrict__ zeros,
+                                                               uint8_t* __restrict__ codes_p, float* __restrict__ err) {
+  __shared__ __attribute__((aligned(16))) float Ul[kBlock][4][QP];
+  __shared__ float inv_d[kBlock];
+  const int e = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int j0 = blk * kBlock;
+  const float* Ub = U + static_cast<int64_t>(e) * bsu + static_cast<int64_t>(j0) * d_in + j0;
+  // stage the U block: thread handles float4 chunks (row j, columns 4m..4m+3)
+  for (int i = tid; i < kBlock * kBlock / 4; i += 256) {
+    const int j = i >> 5, m = i & 31;
+    const float4 v = *reinterpret_cast<const float4*>(Ub + static_cast<int64_t>(j) * d_in + 4 * m);
+    Ul[j][0][m] = (4 * m + 0 == j) ? 0.0f : v.x;
+    Ul[j][1][m] = (4 * m + 1 == j) ? 0.0f : v.y;
+    Ul[j][2][m] = (4 * m + 2 == j) ? 0.0f : v.z;
+    Ul[j][3][m] = (4 * m + 3 == j) ? 0.0f : v.w;
+    if (4 * m <= j && j < 4 * m + 4) {
+      const float dj = (j == 4 * m) ? v.x : (j == 4 * m + 1) ? v.y : (j == 4 * m + 2) ? v.z : v.w;
+      inv_d[j] = 1.0f / dj;
+    }
+  }
+  __syncthreads();
+  const int r = blockIdx.x * 64 + (tid >> 2);
+  const int k = tid & 3;
+  if (r >= d_out) return;
+  const int n_groups = G ? d_in / G : 1;
+  const float* wrow = Wp + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
+  float w[32];
+#pragma unroll
+  for (int m = 0; m < 32; ++m) w[m] = wrow[4 * m + k];
+  float* sc = scales + static_cast<int64_t>(e) * n_groups * d_out;
+  uint8_t* zr = zeros + static_cast<int64_t>(e) * n_groups * d_out;
+  float s = 1.0f, z = 0.0f, inv_s = 1.0f;
+  if constexpr (G == 0) {
+    s = sc[r];
+    z = static_cast<float>(zr[r]);
+    inv_s = 1.0f / s;
+  }
+  uint32_t cw[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) cw[i] = 0u;
+  const float* ul_k = &Ul[0][k][0];
+
+#pragma unroll
+  for (int j = 0; j < kBlock; ++j) {
+    const int mj = j >> 2;
+    if constexpr (G != 0) {
+      if (j % G == 0) {
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int m = j / 4; m < (j + G) / 4; ++m) {
+          lo = fminf(lo, w[m]);
+          hi = fmaxf(hi, w[m]);
+        }
+        lo = quad_min(lo);
+        hi = quad_max(hi);
+        s = fmaxf((hi - lo) / maxq, 1e-8f);
+        z = rintf(-lo / s);
+        inv_s = 1.0f / s;
+        if (k == 0) {
+          const int gi = (j0 + j) / G;
+          sc[static_cast<int64_t>(gi) * d_out + r] = s;
+          zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
+        }
+      }
+    }
+    float wj;
+    switch (j & 3) {
+      case 0: wj = quad_bcast<0>(w[mj]); break;
+      case 1: wj = quad_bcast<1>(w[mj]); break;
+      case 2: wj = quad_bcast<2>(w[mj]); break;
+      default: wj = quad_bcast<3>(w[mj]); break;
+    }
+    const float q = fminf(fmaxf(rintf(wj * inv_s) + z, 0.0f), maxq);
+    const float wq = s * (q - z);
+    const float e_j = (wj - wq) * inv_d[j];
+    cw[j >> 2] |= static_cast<uint32_t>(q) << (8 * (j & 3));
+    // update this lane's columns 4m + k > j (the LDS factor is zero for columns <= j)
+    const float* urow = ul_k + j * (4 * QP);
+#pragma unroll
+    for (int m = mj; m < 32; ++m) w[m] = fmaf(-e_j, urow[m], w[m]);
+    if (k == (j & 3)) w[mj] = e_j;   // the owner keeps err_j in place of w_j
+  }
+  // codes: every lane holds all 128; lane k stores words [8k, 8k+8)
+  uint32_t* cdst = reinterpret_cast<uint32_t*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
+  // lane-dependent word choice by masks (keeps cw[] in registers; no dynamic indexing)
+  const uint32_t m0 = k == 0 ? ~0u : 0u, m1 = k == 1 ? ~0u : 0u, m2 = k == 2 ? ~0u : 0u, m3 = k == 3 ? ~0u : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    cdst[8 * k + i] = (cw[i] & m0) | (cw[8 + i] & m1) | (cw[16 + i] & m2) | (cw[24 + i] & m3);
+  float* edst = err + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
+#pragma unroll
+  for (int m = 0; m < 32; ++m) edst[4 * m + k] = w[m];
 }
 
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p,
@@ -173,7 +296,7 @@ QuantWs carve(void* ws, int batch, int d_out, int d_in) {
   QuantWs w{};
   const size_t rows = static_cast<size_t>(batch) * d_out;
   w.Wp = cv.take<float>(rows * d_in);
-  w.err = cv.take<float>(rows * kBlock);
+  w.err = cv.take<float>(rows * d_in);
   w.codes_p = cv.take<uint8_t>(rows * d_in);
   w.inv = cv.take<int32_t>(static_cast<size_t>(batch) * d_in);
   w.bytes = cv.used;
@@ -184,9 +307,44 @@ template <int G>
 gptq_status launch_sweep(dim3 grid, hipStream_t stream, const float* Wp, const float* U, int64_t bsu, int d_out,
                          int d_in, int blk, float maxq, float* scales, uint8_t* zeros, uint8_t* codes_p,
                          float* err) {
-  GPTQ_LAUNCH(block_sweep_kernel<G>, grid, dim3(64), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales,
+  GPTQ_LAUNCH(block_sweep_quad_kernel<G>, grid, dim3(256), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales,
               zeros, codes_p, err);
   return GPTQ_OK;
+}
+
+gptq_status sweep_block(int b, int G, dim3 sg, hipStream_t stream, int d_out, int d_in, const QuantWs& w,
+                        const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
+  switch (G) {
+    case 0: return launch_sweep<0>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 16: return launch_sweep<16>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 32: return launch_sweep<32>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 64: return launch_sweep<64>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 128: return launch_sweep<128>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    default: return GPTQ_ERR_UNSUPPORTED;
+  }
+}
+
+// Blocks [b0, b1) of the sweep.  The lazy batch update is applied hierarchically: after
+// the left half of a range is swept, its errors are pushed into the right half of the
+// same range in one product, W_p[:, right] -= Err[:, left] @ U[left, right].  Every pair
+// of columns j < k in different blocks meets exactly once, at the range where they are
+// split, after j's error is known and before k is quantized, so the updates are the same
+// as applying each block's errors to all later columns right after the block; only the
+// time at which they land changes.  Most of the flops move into a few large products.
+gptq_status sweep_range(int b0, int b1, int G, dim3 sg, hipStream_t stream, int batch, int d_out, int d_in,
+                        const QuantWs& w, const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
+  if (b1 - b0 == 1) return sweep_block(b0, G, sg, stream, d_out, d_in, w, U, bsu, maxq, scales, zeros);
+  const int bm = b0 + (b1 - b0) / 2;
+  gptq_status st = sweep_range(b0, bm, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales, zeros);
+  if (st != GPTQ_OK) return st;
+  GemmArgs g{};
+  g.M = d_out; g.N = (b1 - bm) * kBlock; g.K = (bm - b0) * kBlock;
+  g.A = w.err + static_cast<int64_t>(b0) * kBlock; g.lda = d_in; g.sA = static_cast<int64_t>(d_out) * d_in;
+  g.B = U + static_cast<int64_t>(b0) * kBlock * d_in + static_cast<int64_t>(bm) * kBlock; g.ldb = d_in; g.sB = bsu;
+  g.C = w.Wp + static_cast<int64_t>(bm) * kBlock; g.ldc = d_in; g.sC = static_cast<int64_t>(d_out) * d_in;
+  g.alpha = -1.0f; g.beta = 1.0f; g.transB = 0; g.flags = 0; g.batch = batch;
+  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
+  return sweep_range(bm, b1, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales, zeros);
 }
 
 }  // namespace
@@ -226,30 +384,9 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
     GPTQ_LAUNCH(row_grid_kernel, dim3(d_out, batch), blk, 0, stream, w.Wp, d_out, d_in, maxq, scales, zeros);
   }
   const dim3 sg((d_out + 63) / 64, batch);
-  const int nblk = d_in / kBlock;
-  for (int b = 0; b < nblk; ++b) {
-    gptq_status st;
-    switch (G) {
-      case 0: st = launch_sweep<0>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err); break;
-      case 16: st = launch_sweep<16>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err); break;
-      case 32: st = launch_sweep<32>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err); break;
-      case 64: st = launch_sweep<64>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err); break;
-      case 128: st = launch_sweep<128>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err); break;
-      default: return GPTQ_ERR_UNSUPPORTED;
-    }
-    if (st != GPTQ_OK) return st;
-    const int j2 = (b + 1) * kBlock;
-    if (j2 < d_in) {
-      GemmArgs g{};
-      g.M = d_out; g.N = d_in - j2; g.K = kBlock;
-      g.A = w.err; g.lda = kBlock; g.sA = static_cast<int64_t>(d_out) * kBlock;
-      g.B = U + static_cast<int64_t>(b) * kBlock * d_in + j2; g.ldb = d_in; g.sB = bsu;
-      g.C = w.Wp + j2; g.ldc = d_in; g.sC = static_cast<int64_t>(d_out) * d_in;
-      g.alpha = -1.0f; g.beta = 1.0f; g.transB = 0; g.flags = 0; g.batch = batch;
-      st = gemm_f32(g, stream);
-      if (st != GPTQ_OK) return st;
-    }
-  }
+  const gptq_status st = sweep_range(0, d_in / kBlock, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales,
+                                     zeros);
+  if (st != GPTQ_OK) return st;
   GPTQ_LAUNCH(unpermute_kernel, pg, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G, codes, g_idx);
   return GPTQ_OK;
 }
