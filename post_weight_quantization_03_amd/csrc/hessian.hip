@@ -4,19 +4,23 @@
 // in X X^T, so one d_in x d_in Hessian serves every row; "GPTQ Architecture, in depth",
 // "The algorithm in code": it is accumulated per calibration batch.
 //
-// bf16/fp16 inputs: a symmetric rank-k update on the MFMA units.  Each workgroup owns a
-// 256 x 256 tile on or below the diagonal and a slice of the tokens; products of two
+// bf16/fp16 inputs: a symmetric rank-k update on the MFMA units.  Each workgroup (8 waves)
+// owns a 256 x 256 tile on or below the diagonal and a slice of the tokens; products of two
 // 16-bit values are exact in fp32 and are summed in fp32 by v_mfma_f32_32x32x16_{bf16,f16}.
-// Token-major X is staged through LDS transposed (channel-major, 8 tokens per MFMA
-// operand), double-buffered so global loads of the next stage overlap the MFMAs.
+// Token-major X is copied to LDS as it lies in memory by direct global->LDS loads (no
+// register staging; XOR-swizzled 16-byte chunks), with three stages in flight
+// under the MFMAs; the MFMA operands (8 consecutive tokens of one channel per
+// lane) come out of LDS through the transposing ds_read_b64_tr_b16.
 // Off-diagonal tiles are mirrored into the upper triangle, so H is exactly symmetric.
-// When the tiles alone cannot fill the 256 CUs the tokens are split and the fp32
-// partial tiles are summed in a fixed order by a second kernel (deterministic, no
-// atomics).  fp32 inputs use a plain FMA tile kernel (small layers only).
+// When the tiles alone cannot fill the 256 CUs the tokens are split and the fp32 partial
+// tiles are summed in a fixed order by a second kernel (deterministic, no atomics).
+// fp32 inputs use a plain FMA tile kernel (small layers only).
 //
-// The fp64 diagonal key 2 * sum_t x^2 (exact products, fp64 sums) is accumulated by its
-// own kernel pair: it decides the ActOrder permutation, where fp32 sums are not precise
-// enough to order nearly equal channels reproducibly.
+// The fp64 diagonal key 2 * sum_t x^2 (exact products, fp64 sums) decides the ActOrder
+// permutation, where fp32 sums are not precise enough to order nearly equal channels
+// reproducibly.  For 16-bit inputs the diagonal-tile workgroups accumulate it from the
+// LDS stages they already hold; fp32 inputs use a separate kernel.  Per-slice fp64
+// partials are summed in a fixed order.
 #include <algorithm>
 
 #include "common.h"
@@ -26,8 +30,9 @@ namespace {
 
 constexpr int ST = 256;        // output tile edge
 constexpr int SBK = 32;        // tokens per LDS stage
-constexpr int LDK = SBK + 4;   // LDS row (one channel) length in 16-bit elements
-constexpr int SYRK_THREADS = 256;
+constexpr int NBUF = 4;        // LDS stage buffers per operand
+constexpr int DEPTH = 3;       // stages in flight ahead of the one being multiplied
+constexpr int SYRK_THREADS = 512;   // 8 waves: 2 (rows) x 4 (columns) of 128 x 64
 constexpr int kMinTokensPerSplit = 2048;
 
 __device__ __forceinline__ void lower_tile_coords(int t, int& I, int& J) {
@@ -39,143 +44,248 @@ __device__ __forceinline__ void lower_tile_coords(int t, int& I, int& J) {
   J = t - i * (i + 1) / 2;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes
+// land at LDS address lds_base + 16 l; lds_base must be wave-uniform.  Issued from inline
+// assembly so that the compiler does not fence every later LDS read on it; the caller
+// waits for completion with s_waitcnt vmcnt.  m0 is saved and restored around the copy.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
+  // the address is wave-uniform by contract; readfirstlane makes that visible to the compiler
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(lds_dst))));
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
 template <bool kF16>
-__device__ __forceinline__ f32x16 mfma16(const uint2 a[2], const uint2 b[2], f32x16 c) {
-  uint4 av = make_uint4(a[0].x, a[0].y, a[1].x, a[1].y);
-  uint4 bv = make_uint4(b[0].x, b[0].y, b[1].x, b[1].y);
+__device__ __forceinline__ f32x16 mfma16(s16x4 a0, s16x4 a1, s16x4 b0, s16x4 b1, f32x16 c) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  const s16x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   if constexpr (kF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
-                                                  __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
   } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                   __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
   }
 }
 
-// One 256x256 lower tile (blockIdx.x), token slice (blockIdx.y), problem (blockIdx.z).
-// partial == nullptr: H += 2 * tile (and its mirror).  Otherwise the raw tile is stored
-// to partial[e][split][tile][256][256] for syrk_reduce_kernel.
+// LDS stage layout: SBK token rows of 256 channels (512 bytes), stored as 32 chunks of 16
+// bytes; chunk c of row t sits at physical position c ^ (2 * (t & 3)) so that the four
+// consecutive token rows read together by the transposing loads hit different banks.
+__device__ __forceinline__ int swz_chunk(int t, int c) { return c ^ (2 * (t & 3)); }
+
+// One 256x256 lower tile and token slice per workgroup of 8 waves (2 x 4 waves of 128 x 64).
+// (tile, slice) pairs are assigned so that each XCD (workgroups are dealt to the 8 XCDs
+// round-robin) works through a contiguous run of tiles of the same slice, which share
+// operand blocks in its L2.
+//
+// Global->LDS copies run DEPTH stages ahead of the math, and within the math the operand
+// reads (transposing LDS reads) of the next 16-token half stage are in flight while the
+// MFMAs of the current one issue, so neither the copies nor the LDS reads serialise with
+// the matrix cores.
+//
+// partial == nullptr: H += 2 * tile (and its mirror).  Otherwise the raw tile goes to
+// partial[e][slice][tile][256][256] for syrk_reduce_kernel.  Diagonal tiles also add the
+// fp64 channel energies sum_t x^2 of their 256 channels to epart[e][slice][c].
 template <bool kF16>
 __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, int d_in,
-    int64_t tokens_per_split, float* __restrict__ H, int64_t bsh, float* __restrict__ partial,
-    int ntiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][ST * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][ST * LDK];
+    int64_t tokens_per_split, int ksplit, float* __restrict__ H, int64_t bsh, float* __restrict__ partial,
+    double* __restrict__ epart, int ntiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][SBK * ST];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][SBK * ST];
 
-  const int e = blockIdx.z;
-  const int split = blockIdx.y;
+  // (tile, slice) of this workgroup: bijection from the linear id that keeps each XCD's
+  // share contiguous.
+  const int e = blockIdx.y;
+  const int total = ntiles * ksplit;
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int base_n = total >> 3, extra = total & 7;
+  const int idx = xcd * base_n + min(xcd, extra) + slot;
+  const int split = idx / ntiles;
+  const int tile = idx - split * ntiles;
   int I, J;
-  lower_tile_coords(blockIdx.x, I, J);
+  lower_tile_coords(tile, I, J);
   const bool diag = (I == J);
   const int I0 = I * ST, J0 = J * ST;
   const int64_t t_begin = static_cast<int64_t>(split) * tokens_per_split;
   const int64_t t_end = min(n_tokens, t_begin + tokens_per_split);
   const uint16_t* Xe = X + static_cast<int64_t>(e) * bsx;
+  const bool full_cols = (I0 + ST <= d_in) && (J0 + ST <= d_in);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // loader unit of a thread: tokens [4*lq, 4*lq+4) of the stage, channels [8*loct, 8*loct+8)
-  const int lq = tid & 7, loct = tid >> 3;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  uint4 ra[4], rb[4];
-  auto gload = [&](int64_t t0, int C0, uint4* r) {
-    const int c = C0 + 8 * loct;
+  // Stage loader.  Fast path (all 32 rows and all 256 channels valid): each wave issues 2
+  // direct global->LDS copies of 2 token rows (64 lanes x 16 bytes, lane-linear in LDS)
+  // per operand; lane l fills physical chunk l%32 of its row, i.e. fetches logical chunk
+  // (l%32) ^ swizzle.  Tail stages go through registers with zero fill.
+  auto load_stage = [&](int64_t t0, int C0, uint16_t* dst) {
+    const int rows = static_cast<int>(min<int64_t>(SBK, t_end - t0));
+    if (rows == SBK && full_cols) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t t = t0 + 4 * lq + k;
-      if (t < t_end && c < d_in) {
-        r[k] = *reinterpret_cast<const uint4*>(Xe + t * ldx + c);
-      } else {
-        r[k] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < 2; ++i) {
+        const int r = 4 * wave + 2 * i + (lane >> 5);
+        const int c = swz_chunk(r, lane & 31);
+        lds_dma16(Xe + (t0 + r) * ldx + C0 + 8 * c, dst + (4 * wave + 2 * i) * ST);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 4 * wave + 2 * i + (lane >> 5);
+        const int p = lane & 31;
+        const int c = swz_chunk(r, p);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < rows && C0 + 8 * c < d_in) v = *reinterpret_cast<const uint4*>(Xe + (t0 + r) * ldx + C0 + 8 * c);
+        *reinterpret_cast<uint4*>(dst + r * ST + 8 * p) = v;
       }
     }
   };
-  // Transpose 4 tokens x 8 channels in registers: channel i gets its 4 tokens as 8 bytes.
-  auto swrite = [&](uint16_t* s, const uint4* r) {
-    const uint32_t w[4][4] = {{r[0].x, r[0].y, r[0].z, r[0].w},
-                              {r[1].x, r[1].y, r[1].z, r[1].w},
-                              {r[2].x, r[2].y, r[2].z, r[2].w},
-                              {r[3].x, r[3].y, r[3].z, r[3].w}};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(w[1][i >> 1], w[0][i >> 1], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(w[3][i >> 1], w[2][i >> 1], sel);
-      *reinterpret_cast<uint2*>(s + (8 * loct + i) * LDK + 4 * lq) = make_uint2(lo, hi);
-    }
-  };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  const int am = lane & 31, ak = (lane >> 5) * 8;
+  // transposing-read coordinates of this lane within a 32x16 operand block
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int rq = j16 >> 2, ra = j16 & 3;
+  const int op_ch = 16 * (g16 & 1) + 4 * ra;         // + 32*block
+  const int op_tok = 8 * (g16 >> 1) + rq;            // + 16*ks + 4*half
   const int nstages = static_cast<int>((t_end - t_begin + SBK - 1) / SBK);
+  double energy = 0.0;                               // diagonal tiles: channel I0 + tid
 
+  auto operand = [&](const uint16_t* stage, int ch0, int tok0) -> s16x4 {
+    const int ch = ch0 + op_ch;
+    const int t = tok0 + op_tok;
+    const int byte = t * (2 * ST) + 16 * swz_chunk(t, ch >> 3) + 2 * (ch & 7);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(reinterpret_cast<const char*>(stage) + byte));
+  };
+
+  // Copies in flight per wave per stage (the fast path; tail stages load through
+  // registers and are complete when issued).  Waiting for a stage means allowing the
+  // copies of the `later` stages issued after it to stay outstanding.
+  auto wait_copies = [&](int later) {
+    const int n = later * (diag ? 2 : 4);
+    switch (n) {
+      case 0: wait_vmcnt<0>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 6: wait_vmcnt<6>(); break;
+      default: wait_vmcnt<8>(); break;
+    }
+  };
+  // operands of one 16-token half stage
+  struct Ops {
+    s16x4 a0[4], a1[4], b0[2], b1[2];
+  };
+  auto read_ops = [&](int stage, int ks, Ops& o) {
+    const uint16_t* as = sA[stage % NBUF];
+    const uint16_t* bs = diag ? as : sB[stage % NBUF];
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      o.a0[bm] = operand(as, 128 * wm + 32 * bm, 16 * ks);
+      o.a1[bm] = operand(as, 128 * wm + 32 * bm, 16 * ks + 4);
+    }
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) {
+      o.b0[bn] = operand(bs, 64 * wn + 32 * bn, 16 * ks);
+      o.b1[bn] = operand(bs, 64 * wn + 32 * bn, 16 * ks + 4);
+    }
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = mfma16<kF16>(o.a0[bm], o.a1[bm], o.b0[bn], o.b1[bn], acc[bm][bn]);
+    // keep the MFMAs ahead of the following wait/barrier (the compiler would otherwise sink
+    // them below it and serialise them with the operand reads)
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) asm volatile("" : "+v"(acc[bm][bn]));
+  };
+
+  for (int k = 0; k < DEPTH && k < nstages; ++k) {
+    const int64_t tk = t_begin + static_cast<int64_t>(k) * SBK;
+    load_stage(tk, I0, sA[k]);
+    if (!diag) load_stage(tk, J0, sB[k]);
+  }
+  Ops P, Q;   // half-stage operand sets: P = (stage, first half), Q = (stage, second half)
   if (nstages > 0) {
-    gload(t_begin, I0, ra);
-    if (!diag) gload(t_begin, J0, rb);
-    swrite(sA[0], ra);
-    if (!diag) swrite(sB[0], rb);
-  }
-  __syncthreads();
-
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    const bool more = (s + 1 < nstages);
-    if (more) {
-      const int64_t tn = t_begin + static_cast<int64_t>(s + 1) * SBK;
-      gload(tn, I0, ra);
-      if (!diag) gload(tn, J0, rb);
-    }
-    const uint16_t* as = sA[buf];
-    const uint16_t* bs = diag ? sA[buf] : sB[buf];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint2 av[4][2], bv[4][2];
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        const uint16_t* p = as + (128 * wm + 32 * bm + am) * LDK + 16 * ks + ak;
-        av[bm][0] = *reinterpret_cast<const uint2*>(p);
-        av[bm][1] = *reinterpret_cast<const uint2*>(p + 4);
-      }
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
-        const uint16_t* p = bs + (128 * wn + 32 * bn + am) * LDK + 16 * ks + ak;
-        bv[bn][0] = *reinterpret_cast<const uint2*>(p);
-        bv[bn][1] = *reinterpret_cast<const uint2*>(p + 4);
-      }
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma16<kF16>(av[bm], bv[bn], acc[bm][bn]);
-    }
-    if (more) {
-      swrite(sA[buf ^ 1], ra);
-      if (!diag) swrite(sB[buf ^ 1], rb);
-    }
+    wait_copies(min(DEPTH, nstages) - 1);
     __syncthreads();
+    read_ops(0, 0, P);
   }
+  // Each stage runs in two phases; in each, the MFMAs of one half stage are issued while
+  // the operand reads of the next half stage are in flight:
+  //   phase 1: read (s, second half) | MFMAs (s, first half) ; wait for stage s+1, barrier;
+  //            start the copy of stage s+DEPTH into the buffer of stage s-1 (every wave is
+  //            past the barrier, so done with stage s-1)
+  //   phase 2: read (s+1, first half) | MFMAs (s, second half)
+  for (int s = 0; s < nstages; ++s) {
+    read_ops(s, 1, Q);
+    if (diag && epart != nullptr && tid < ST) {
+      // fp64 energy of channel I0 + tid over this stage's tokens (products exact in fp64)
+      const uint16_t* as = sA[s % NBUF];
+      const int ch = tid;
+#pragma unroll 8
+      for (int t = 0; t < SBK; ++t) {
+        const uint16_t v = as[t * ST + 8 * swz_chunk(t, ch >> 3) + (ch & 7)];
+        const double x = static_cast<double>(kF16 ? f16_to_f32(v) : bf16_to_f32(v));
+        energy = fma(x, x, energy);
+      }
+    }
+    mma(P);
+    if (s + 1 < nstages) wait_copies(min(s + DEPTH - 1, nstages - 1) - (s + 1));
+    __syncthreads();
+    if (s + DEPTH < nstages) {
+      const int64_t tn = t_begin + static_cast<int64_t>(s + DEPTH) * SBK;
+      load_stage(tn, I0, sA[(s + DEPTH) % NBUF]);
+      if (!diag) load_stage(tn, J0, sB[(s + DEPTH) % NBUF]);
+    }
+    if (s + 1 < nstages) read_ops(s + 1, 0, P);
+    mma(Q);
+  }
+  if (diag && epart != nullptr && tid < ST && I0 + tid < d_in)
+    epart[(static_cast<int64_t>(e) * ksplit + split) * d_in + I0 + tid] = energy;
 
   // Accumulator layout of a 32x32 MFMA block: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (partial != nullptr) {
-    float* P = partial + ((static_cast<int64_t>(e) * gridDim.y + split) * ntiles + blockIdx.x) *
-                             static_cast<int64_t>(ST * ST);
+    float* P = partial + ((static_cast<int64_t>(e) * ksplit + split) * ntiles + tile) * static_cast<int64_t>(ST * ST);
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
+      for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = 128 * wm + 32 * bm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int n = 128 * wn + 32 * bn + (lane & 31);
+          const int n = 64 * wn + 32 * bn + (lane & 31);
           P[m * ST + n] = acc[bm][bn][r];
         }
     return;
@@ -184,11 +294,11 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
+    for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int m0 = 128 * wm + 32 * bm + 8 * rq + 4 * (lane >> 5);
-        const int n = 128 * wn + 32 * bn + (lane & 31);
+      for (int rq4 = 0; rq4 < 4; ++rq4) {
+        const int m0 = 128 * wm + 32 * bm + 8 * rq4 + 4 * (lane >> 5);
+        const int n = 64 * wn + 32 * bn + (lane & 31);
         const int col = J0 + n;
         if (col >= d_in) continue;
 #pragma unroll
@@ -196,7 +306,7 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
           const int m = m0 + q;
           const int row = I0 + m;
           if (row >= d_in || (diag && m < n)) continue;
-          const float v = 2.0f * acc[bm][bn][4 * rq + q];
+          const float v = 2.0f * acc[bm][bn][4 * rq4 + q];
           He[static_cast<int64_t>(row) * d_in + col] += v;
           if (!diag || m > n) He[static_cast<int64_t>(col) * d_in + row] += v;
         }
@@ -363,6 +473,11 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
     pl.ksplit = static_cast<int>((n_tokens + pl.kchunk - 1) / pl.kchunk);
     if (pl.ksplit < 1) pl.ksplit = 1;
   }
+  if (mfma) {
+    pl.esplit = pl.ksplit;
+    pl.echunk = pl.kchunk;
+    return pl;
+  }
   const int cblocks = (d_in + 255) / 256;
   const int64_t ewant = (2048 + static_cast<int64_t>(cblocks) * batch - 1) /
                         (static_cast<int64_t>(cblocks) * batch);
@@ -411,38 +526,26 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
 
   const dim3 blk(256);
   if (mfma) {
-    const dim3 grid(pl.ntiles, pl.ksplit, batch);
+    const dim3 sblk(SYRK_THREADS);
+    const dim3 grid(pl.ntiles * pl.ksplit, batch);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     float* part = pl.ksplit > 1 ? partial : nullptr;
     if (x_dtype == GPTQ_F16) {
-      GPTQ_LAUNCH(syrk_mfma_kernel<true>, grid, blk, 0, stream, Xh, ldx, bsx, n_tokens, d_in,
-                  pl.kchunk, H, bsh, part, pl.ntiles);
+      GPTQ_LAUNCH(syrk_mfma_kernel<true>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit, H,
+                  bsh, part, epart, pl.ntiles);
     } else {
-      GPTQ_LAUNCH(syrk_mfma_kernel<false>, grid, blk, 0, stream, Xh, ldx, bsx, n_tokens, d_in,
-                  pl.kchunk, H, bsh, part, pl.ntiles);
+      GPTQ_LAUNCH(syrk_mfma_kernel<false>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
+                  H, bsh, part, epart, pl.ntiles);
     }
     if (pl.ksplit > 1) {
-      GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial,
-                  pl.ksplit, pl.ntiles, d_in, H, bsh);
+      GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
+                  H, bsh);
     }
   } else {
-    GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream,
-                static_cast<const float*>(X), ldx, bsx, n_tokens, d_in, H, bsh);
-  }
-  const dim3 eg((d_in + 255) / 256, pl.esplit, batch);
-  switch (x_dtype) {
-    case GPTQ_F32:
-      GPTQ_LAUNCH(channel_energy_kernel<float>, eg, blk, 0, stream, static_cast<const float*>(X), ldx,
-                  bsx, n_tokens, d_in, pl.echunk, epart);
-      break;
-    case GPTQ_BF16:
-      GPTQ_LAUNCH(channel_energy_kernel<BF16>, eg, blk, 0, stream, static_cast<const BF16*>(X), ldx,
-                  bsx, n_tokens, d_in, pl.echunk, epart);
-      break;
-    case GPTQ_F16:
-      GPTQ_LAUNCH(channel_energy_kernel<F16>, eg, blk, 0, stream, static_cast<const F16*>(X), ldx,
-                  bsx, n_tokens, d_in, pl.echunk, epart);
-      break;
+    GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream, static_cast<const float*>(X), ldx, bsx,
+                n_tokens, d_in, H, bsh);
+    GPTQ_LAUNCH(channel_energy_kernel<float>, dim3((d_in + 255) / 256, pl.esplit, batch), blk, 0, stream,
+                static_cast<const float*>(X), ldx, bsx, n_tokens, d_in, pl.echunk, epart);
   }
   GPTQ_LAUNCH(channel_energy_reduce_kernel, dim3((d_in + 255) / 256, batch), blk, 0, stream, epart,
               pl.esplit, d_in, diag_key, n_seen, n_tokens);
