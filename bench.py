@@ -13,6 +13,7 @@ kernel, CPU-oracle baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,10 +37,35 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="attn_proj")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per accumulate call (0 = all at once)")
+    ap.add_argument("--bits", type=int, default=0, help="override the workload's bit width (e.g. 3 for moe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
                     help="calibration tokens the CPU oracle processes (its Hessian time is scaled up)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="before warmup, run one plain device copy of this many bytes (counter calibration)")
     return ap.parse_args()
+
+
+SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_03_amd", "csrc", "hessian.hip")
+
+
+def syrk_traffic(workload: str):
+    """HBM bytes per SYRK launch from the committed counter summary of this workload, or None
+    when there is none or the SYRK source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"syrk_mfma_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            k, sep, v = line.partition(":")
+            if sep:
+                fields[k.strip()] = v.strip()
+    with open(SYRK_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("hessian.hip sha256") != digest or "traffic bytes per launch" not in fields:
+        return None
+    return int(float(fields["traffic bytes per launch"]))
 
 
 def describe(spec) -> str:
@@ -83,6 +109,8 @@ def main():
     from post_weight_quantization_03_amd import gptq, synth
 
     spec = synth.config(args.config)
+    if args.bits:
+        spec = synth.config(args.config, bits=args.bits)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
@@ -110,6 +138,12 @@ def main():
                        device=dev)
     stream = torch.cuda.current_stream()
     ev = {k: [] for k in ("hessian", "prepare", "quantize", "pack")}
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(record: bool):
         def mark():
@@ -140,22 +174,31 @@ def main():
         step(False)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    gptq.timing_enable(True)
+    gptq.timing_read()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gptq.timing_enable(False)
+    syrk_total_ms, syrk_launches = gptq.timing_read()
     ms = wall * 1e3 / args.steps
     stages = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
     weights = E * spec.d_out * spec.d_in
     value = weights / (ms / 1e3) / 1e9
 
-    # dominant kernel: the Hessian SYRK (algorithmic flops = symmetric half, d_in (d_in+1) n per layer)
-    syrk_flops = E * spec.d_in * (spec.d_in + 1) * spec.n_tokens
-    syrk_ms = stages["hessian"]
+    # Dominant kernel: the Hessian SYRK.  Algorithmic flops = the lower triangle with its
+    # diagonal, 2 * d_in (d_in + 1) / 2 per token and layer; one launch covers one accumulate call.
+    launches_per_step = (spec.n_tokens + chunk - 1) // chunk
+    syrk_flops = E * spec.d_in * (spec.d_in + 1) * min(chunk, spec.n_tokens)
+    syrk_ms = syrk_total_ms / max(syrk_launches, 1)
     achieved = syrk_flops / (syrk_ms / 1e3) / 1e12
-    roof = dict(bound="mfma", kernel="syrk_mfma_kernel (accumulate call)", achieved=round(achieved, 2),
-                peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None)
+    peak = PEAK_BF16_TFLOPS if spec.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
+    roof = dict(bound="mfma", kernel="syrk_mfma_kernel", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                frac=round(achieved / peak, 4), traffic=syrk_traffic(spec.name) if chunk >= spec.n_tokens else None,
+                launch_ms=round(syrk_ms, 4), launches=syrk_launches, launches_per_step=launches_per_step,
+                flops_per_launch=syrk_flops)
     out = dict(metric=METRIC, value=round(value, 4), unit="Gweights/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="bf16->f32", data="synthetic",

@@ -176,6 +176,15 @@ gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const u
 size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
                            int64_t n_tokens_hint, const gptq_params* p);
 
+/* Measurement hook for the Hessian SYRK kernel (the dominant kernel of the path).
+ * While enabled (on != 0), every gptq_accumulate_hessian call records a pair of HIP events
+ * on its stream immediately around its SYRK kernel launch.  gptq_timing_read waits for the
+ * recorded events, returns the summed elapsed milliseconds and the number of launches since
+ * the previous read, and forgets them.  Events are created by the library on first use and
+ * reused; the hook is process-wide and not meant for concurrent callers. */
+gptq_status gptq_timing_enable(int on);
+gptq_status gptq_timing_read(double* total_ms, int64_t* launches);
+
 /* Static description of a status code. */
 const char* gptq_status_string(gptq_status s);
 

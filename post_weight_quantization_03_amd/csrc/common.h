@@ -88,6 +88,10 @@ gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uin
                          const float* scales, const uint8_t* zeros, int32_t* qweight, int32_t* qzeros,
                          uint16_t* scales_f16, hipStream_t stream);
 
+// SYRK launch timing (gptq_timing_enable / gptq_timing_read): returns the event pair to
+// record around the next SYRK launch, or nulls when timing is off.
+void timing_pair(hipEvent_t* start, hipEvent_t* stop);
+
 // fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C (row-major, batched by blockIdx.z).
 struct GemmArgs {
   int M, N, K;

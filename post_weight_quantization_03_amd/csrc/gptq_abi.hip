@@ -1,6 +1,9 @@
 // C ABI of libgptq: argument validation and dispatch to the kernel enqueuers.
 // Every function declared in include/gptq.h is defined here.
 #include <cmath>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "common.h"
 
@@ -27,9 +30,67 @@ gptq_status check_params(const gptq_params* p, int d_in, bool need_grid) {
   return GPTQ_OK;
 }
 
+// SYRK timing state: recorded (start, stop) pairs and a pool of reusable events.
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded, pool;
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
 }  // namespace
 
+namespace gptq {
+void timing_pair(hipEvent_t* start, hipEvent_t* stop) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  *start = *stop = nullptr;
+  if (!t.on) return;
+  std::pair<hipEvent_t, hipEvent_t> p{nullptr, nullptr};
+  if (!t.pool.empty()) {
+    p = t.pool.back();
+    t.pool.pop_back();
+  } else if (hipEventCreate(&p.first) != hipSuccess || hipEventCreate(&p.second) != hipSuccess) {
+    return;
+  }
+  t.recorded.push_back(p);
+  *start = p.first;
+  *stop = p.second;
+}
+}  // namespace gptq
+
 extern "C" {
+
+gptq_status gptq_timing_enable(int on) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_timing_read(double* total_ms, int64_t* launches) {
+  if (total_ms == nullptr || launches == nullptr) return GPTQ_ERR_INVALID_ARG;
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  double sum = 0.0;
+  gptq_status st = GPTQ_OK;
+  for (auto& p : t.recorded) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.second) != hipSuccess || hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) {
+      st = GPTQ_ERR_HIP;
+    }
+    sum += ms;
+    t.pool.push_back(p);
+  }
+  *total_ms = sum;
+  *launches = static_cast<int64_t>(t.recorded.size());
+  t.recorded.clear();
+  return st;
+}
+
 
 gptq_status gptq_accumulate_hessian(int batch, int d_in, int64_t n_tokens, gptq_dtype x_dtype, const void* X,
                                     int64_t ldx, int64_t batch_stride_x, float* H, int64_t batch_stride_h,

@@ -530,6 +530,9 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     const dim3 grid(pl.ntiles * pl.ksplit, batch);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     float* part = pl.ksplit > 1 ? partial : nullptr;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    timing_pair(&ev0, &ev1);
+    if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
       GPTQ_LAUNCH(syrk_mfma_kernel<true>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit, H,
                   bsh, part, epart, pl.ntiles);
@@ -537,6 +540,7 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
       GPTQ_LAUNCH(syrk_mfma_kernel<false>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
                   H, bsh, part, epart, pl.ntiles);
     }
+    if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
     if (pl.ksplit > 1) {
       GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
                   H, bsh);

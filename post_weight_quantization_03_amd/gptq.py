@@ -25,7 +25,7 @@ GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_HIP, GPTQ_ERR_WORKSPAC
 WS_HESSIAN, WS_PREPARE, WS_QUANTIZE = 0, 1, 2
 
 EXPORTED = ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_int4",
-            "gptq_workspace_size", "gptq_status_string", "gptq_version")
+            "gptq_workspace_size", "gptq_status_string", "gptq_version", "gptq_timing_enable", "gptq_timing_read")
 
 
 class GptqError(RuntimeError):
@@ -84,7 +84,10 @@ def lib() -> ctypes.CDLL:
     L.gptq_status_string.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
     L.gptq_version.restype = ctypes.c_char_p
-    for name in ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_int4"):
+    L.gptq_timing_enable.argtypes = [i32]
+    L.gptq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    for name in ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_int4",
+                 "gptq_timing_enable", "gptq_timing_read"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -214,6 +217,18 @@ def pack_int4(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, st
                                 qweight.data_ptr(), qzeros.data_ptr(), sf16.data_ptr(), _stream(stream)),
            "gptq_pack_int4")
     return qweight, qzeros, sf16
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start/stop recording HIP events around every Hessian SYRK kernel launch."""
+    _check(lib().gptq_timing_enable(int(on)), "gptq_timing_enable")
+
+
+def timing_read():
+    """(summed SYRK kernel milliseconds, launches) since the previous read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().gptq_timing_read(ctypes.byref(ms), ctypes.byref(n)), "gptq_timing_read")
+    return ms.value, n.value
 
 
 def gptq_layer(W: torch.Tensor, X_chunks, params: Params, stream=None):

@@ -29,6 +29,13 @@ def test_library_exports_every_declared_symbol():
     assert L.gptq_version().decode().count(".") == 2
 
 
+def test_timing_hook_without_launches():
+    gptq.timing_enable(True)
+    assert gptq.timing_read() == (0.0, 0)
+    gptq.timing_enable(False)
+    assert gptq.lib().gptq_timing_read(None, None) == gptq.GPTQ_ERR_INVALID_ARG
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert gptq.status_string(s)
