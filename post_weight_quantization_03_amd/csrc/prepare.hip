@@ -13,8 +13,8 @@
 //      at 2/3 d^3 instead of 4/3 d^3 flops.
 //
 // Cholesky and inverse together by recursive halving (chol_inv below): one workgroup
-// factors and inverts each 128-column diagonal block in registers/LDS; everything else is
-// fp32 matrix-core products.  A non-positive or non-finite pivot sets a device flag that
+// factors and inverts each 128-column diagonal block in LDS (the same halving, inside the
+// kernel); everything else is fp32 matrix-core products.  A non-positive or non-finite pivot sets a device flag that
 // the host reads back (GPTQ_ERR_NOT_SPD).
 #include <algorithm>
 
@@ -24,7 +24,6 @@ namespace gptq {
 namespace {
 
 constexpr int NB = 128;   // panel width (must equal the GEMM tile)
-constexpr int LP = NB + 1;
 
 // key[c] = diag_key[c], or 1 for a dead input; dead[c] = (diag_key[c] == 0).
 // Also clears the rank counters of actorder_rank_kernel.
@@ -124,150 +123,209 @@ __global__ __launch_bounds__(256) void gather_reversed_kernel(const float* __res
   A[(static_cast<int64_t>(e) * d_in + r) * d_in + c] = v;
 }
 
-// Factor the diagonal block k of A (lower part): writes L_kk into Lbuf and L_kk^-1 into
-// Linv (both full 128x128 blocks, zeros above the diagonal).
+// Factor the diagonal block at (k0, k0) of A: writes L_kk into Lbuf and L_kk^-1 into Linv
+// (full 128x128 blocks, zeros above the diagonal).  Only the lower triangle of A is read.
 //
-// Each of the 256 threads keeps an 8x8 sub-block of the 128x128 block in registers
-// (thread t: block row t/16, block column t%16; a wave covers 32 consecutive rows).
-// Cholesky, right-looking on unscaled columns: at step j every element with
-// j < c, j < i takes a_ic -= a_ij a_cj / a_jj; column j (zeros at rows <= j) and the pivot
-// a_jj are broadcast through LDS by the threads that own them, so each step costs one
-// barrier.  Afterwards l_ij = a_ij / sqrt(a_jj).  The inverse X = L^-1 is then formed the
-// same way, row by row: row k of X is final once divided by l_kk, and every row i > k
-// subtracts l_ik times it.  Loops over columns are unrolled by 8 so that register
-// indices stay compile-time constants.
+// The block and its inverse stay in LDS for the whole kernel, and the same halving as
+// chol_inv below runs inside it down to 16-column leaves:
+//   node(o, S):  node(o, S/2);  L21 = A21 X11^T;  S22 = A22 - L21 L21^T and T = L21 X11;
+//                node(o + S/2, S/2);  X21 = -X22 T
+// (X = L^-1).  A 16-column leaf is factored and inverted by one wave with the 16 rows in
+// lanes 0..15 and the columns in registers; values move between lanes by readlane, so a
+// leaf needs no barrier.  Products are 16x16 output tiles on the fp32 matrix cores,
+// dealt round-robin to the four waves, with one barrier per product.
+constexpr int LLD = NB + 4;   // LDS row stride (floats): 16-byte aligned rows, banks spread
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bcast_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// acc += sum over k in [k0, k1) of A(i0 + i, k) * B(k, j0 + j) for a 16x16 tile, with
+// A(i, k) = pa[i * LLD + k] and B(k, j) = pb[j * LLD + k] (kBT) or pb[k * LLD + j].
+// The K range (a multiple of 16) is split in four contiguous quarters, one per k-slot of
+// the 16x16x4 instruction, so each lane reads its A (and B^T) values 4 at a time.
+template <bool kBT>
+__device__ __forceinline__ f32x4v tile_mma(f32x4v acc, const float* pa, const float* pb, int k0, int k1,
+                                           int lane) {
+  const int kq = (k1 - k0) >> 2;
+  const int q = lane >> 4, rc = lane & 15;
+  const float* ar = pa + rc * LLD + k0 + q * kq;
+  const float* br = kBT ? pb + rc * LLD + k0 + q * kq : pb + (k0 + q * kq) * LLD + rc;
+  for (int s = 0; s < kq; s += 4) {
+    const float4 av = *reinterpret_cast<const float4*>(ar + s);
+    float4 bv;
+    if (kBT) {
+      bv = *reinterpret_cast<const float4*>(br + s);
+    } else {
+      bv = make_float4(br[s * LLD], br[(s + 1) * LLD], br[(s + 2) * LLD], br[(s + 3) * LLD]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// 16x16 tile (rows 4*(lane/16) + r, column lane%16) of a result, to or from LDS.
+__device__ __forceinline__ void tile_store(float* p, f32x4v v, int lane) {
+  float* d = p + 4 * (lane >> 4) * LLD + (lane & 15);
+  d[0] = v[0]; d[LLD] = v[1]; d[2 * LLD] = v[2]; d[3 * LLD] = v[3];
+}
+__device__ __forceinline__ f32x4v tile_load(const float* p, int lane) {
+  const float* s = p + 4 * (lane >> 4) * LLD + (lane & 15);
+  f32x4v v;
+  v[0] = s[0]; v[1] = s[LLD]; v[2] = s[2 * LLD]; v[3] = s[3 * LLD];
+  return v;
+}
+
+// Cholesky and inverse of the 16x16 diagonal block at (o, o), by the calling wave.
+// Lane i < 16 holds row i.  Column k: pivot d = a_kk (from lane k), l_ik = a_ik / sqrt(d),
+// then a_ij -= l_ik l_jk for j > k.  The inverse is formed column per lane: lane j solves
+// L x = e_j by forward substitution with the rows of L read out of lanes 0..15.
+__device__ __forceinline__ void leaf16(float* sA, float* sX, int o, int lane, int* bad) {
+  float a[16];
+  const int r = lane & 15;
+  const float* src = sA + (o + r) * LLD + o;
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(src + c);
+    a[c] = v.x; a[c + 1] = v.y; a[c + 2] = v.z; a[c + 3] = v.w;
+  }
+  float inv_l[16];
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float d = bcast_lane(a[k], k);
+    ok = ok && (d > 0.0f) && (d < INFINITY);
+    const float sq = sqrtf(d);
+    inv_l[k] = 1.0f / sq;
+    a[k] = (r == k) ? sq : a[k] * inv_l[k];
+#pragma unroll
+    for (int j = k + 1; j < 16; ++j) a[j] = fmaf(-a[k], bcast_lane(a[k], j), a[j]);
+  }
+  if (!ok) *bad = 1;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float acc = (r == i) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int k = 0; k < i; ++k) acc = fmaf(-bcast_lane(a[k], i), x[k], acc);
+    x[i] = acc * inv_l[i];
+  }
+  if (lane < 16) {
+    float* dl = sA + (o + r) * LLD + o;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) dl[c] = (c <= r) ? a[c] : 0.0f;
+    float* dx = sX + o * LLD + o + r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dx[i * LLD] = x[i];
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave, int lane, int* bad) {
+  if constexpr (S == 16) {
+    if (wave == 0) leaf16(sA, sX, o, lane, bad);
+    __syncthreads();
+  } else {
+    constexpr int H = S / 2, NT = H / 16, NTT = NT * NT, PER = (NTT + 3) / 4;
+    leaf_node<H>(sA, sX, o, wave, lane, bad);
+    const f32x4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    // L21 = A21 X11^T (X11 lower: k < 16 (tj + 1)), in place over A21
+    f32x4v res[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = wave + 4 * u;
+      if (t < NTT) {
+        const int ti = t / NT, tj = t % NT;
+        res[u] = tile_mma<true>(zero, sA + (o + H + 16 * ti) * LLD + o, sX + (o + 16 * tj) * LLD + o, 0,
+                                16 * (tj + 1), lane);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = wave + 4 * u;
+      if (t < NTT) tile_store(sA + (o + H + 16 * (t / NT)) * LLD + o + 16 * (t % NT), res[u], lane);
+    }
+    __syncthreads();
+    // S22 = A22 - L21 L21^T (lower tiles) and T = L21 X11 (X11 lower: k >= 16 tj) into X21
+    constexpr int NLOW = NT * (NT + 1) / 2;
+    for (int t = wave; t < NLOW + NTT; t += 4) {
+      if (t < NLOW) {
+        int ti = 0;
+        while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+        const int tj = t - ti * (ti + 1) / 2;
+        float* c = sA + (o + H + 16 * ti) * LLD + o + H + 16 * tj;
+        const f32x4v p = tile_mma<true>(zero, sA + (o + H + 16 * ti) * LLD + o, sA + (o + H + 16 * tj) * LLD + o,
+                                        0, H, lane);
+        tile_store(c, tile_load(c, lane) - p, lane);
+      } else {
+        const int u = t - NLOW, ti = u / NT, tj = u % NT;
+        const f32x4v p = tile_mma<false>(zero, sA + (o + H + 16 * ti) * LLD + o, sX + o * LLD + o + 16 * tj,
+                                         16 * tj, H, lane);
+        tile_store(sX + (o + H + 16 * ti) * LLD + o + 16 * tj, p, lane);
+      }
+    }
+    __syncthreads();
+    leaf_node<H>(sA, sX, o + H, wave, lane, bad);
+    // X21 = -X22 T (X22 lower: k < 16 (ti + 1)), in place over T
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = wave + 4 * u;
+      if (t < NTT) {
+        const int ti = t / NT, tj = t % NT;
+        res[u] = tile_mma<false>(zero, sX + (o + H + 16 * ti) * LLD + o + H, sX + (o + H) * LLD + o + 16 * tj, 0,
+                                 16 * (ti + 1), lane);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = wave + 4 * u;
+      if (t < NTT) tile_store(sX + (o + H + 16 * (t / NT)) * LLD + o + 16 * (t % NT), -res[u], lane);
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(256) void potrf_block_kernel(const float* __restrict__ A, float* __restrict__ Lbuf,
                                                           int64_t bsl, float* __restrict__ Linv, int d_in,
                                                           int k0, int* __restrict__ flag) {
-  __shared__ float sL[NB][LP];
-  __shared__ float colbuf[2][NB];
-  __shared__ float piv[NB];
+  __shared__ __attribute__((aligned(16))) float sA[NB * LLD];
+  __shared__ __attribute__((aligned(16))) float sX[NB * LLD];
+  __shared__ int bad;
   const int e = blockIdx.x;
-  const int t = threadIdx.x;
-  const int br = t >> 4, bc = t & 15;
-  const int r0 = 8 * br, c0 = 8 * bc;
-  const int wave_last_row = 32 * (t >> 6) + 31;
-  const float* Ae = A + static_cast<int64_t>(e) * d_in * d_in + static_cast<int64_t>(k0) * d_in + k0;
-
-  float a[8][8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const float4* src = reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(r0 + r) * d_in + c0);
-    const float4 u = src[0], v = src[1];
-    a[r][0] = u.x; a[r][1] = u.y; a[r][2] = u.z; a[r][3] = u.w;
-    a[r][4] = v.x; a[r][5] = v.y; a[r][6] = v.z; a[r][7] = v.w;
-  }
-  // publish column 0
-  if (bc == 0) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) colbuf[0][r0 + r] = (r0 + r > 0) ? a[r][0] : 0.0f;
-    if (br == 0) piv[0] = a[0][0];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  const float* Ae = A + e * dd + static_cast<int64_t>(k0) * d_in + k0;
+  if (t == 0) bad = 0;
+  // 128 rows x 32 float4: thread t loads float4 column t%32 of rows t/32 + 8 m
+#pragma unroll 4
+  for (int m = 0; m < NB / 8; ++m) {
+    const int row = t / 32 + 8 * m, c4 = t % 32;
+    *reinterpret_cast<float4*>(sA + row * LLD + 4 * c4) =
+        *reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(row) * d_in + 4 * c4);
   }
   __syncthreads();
-  for (int jb = 0; jb < NB / 8; ++jb) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = 8 * jb + jj;
-      const int buf = jj & 1;
-      if (wave_last_row > j) {
-        const float rp = 1.0f / piv[j];
-        float ci[8], cc[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) ci[r] = colbuf[buf][r0 + r] * rp;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) cc[c] = colbuf[buf][c0 + c];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) a[r][c] = fmaf(-ci[r], cc[c], a[r][c]);
-      }
-      // publish column j + 1 (its owners are block column (j+1)/8, local column (jj+1)%8)
-      const int jn = j + 1;
-      if (jn < NB && bc == (jn >> 3)) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) colbuf[buf ^ 1][r0 + r] = (r0 + r > jn) ? a[r][(jj + 1) & 7] : 0.0f;
-        if (br == bc) piv[jn] = a[(jj + 1) & 7][(jj + 1) & 7];
-      }
-      __syncthreads();
-    }
-  }
-  // every pivot must be positive and finite
-  if (t == 0) {
-    bool bad = false;
-    for (int j = 0; j < NB; ++j) bad |= !(piv[j] > 0.0f) || !isfinite(piv[j]);
-    if (bad) flag[e] = 1;
-  }
-  // scale: l_ic = a_ic / sqrt(a_cc), l_cc = sqrt(a_cc)
-  float sq[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) sq[c] = sqrtf(piv[c0 + c]);
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int i = r0 + r, cg = c0 + c;
-      const float v = (i > cg) ? a[r][c] / sq[c] : (i == cg ? sq[c] : 0.0f);
-      a[r][c] = v;
-      sL[i][cg] = v;
-    }
-  float* Le = Lbuf + static_cast<int64_t>(e) * bsl + static_cast<int64_t>(k0) * d_in + k0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float4* dst = reinterpret_cast<float4*>(Le + static_cast<int64_t>(r0 + r) * d_in + c0);
-    dst[0] = make_float4(a[r][0], a[r][1], a[r][2], a[r][3]);
-    dst[1] = make_float4(a[r][4], a[r][5], a[r][6], a[r][7]);
-  }
-  // X = L^-1: start from the identity; row 0 of X is e_0 / l_00.
-  float x[8][8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) x[r][c] = (r0 + r == c0 + c) ? 1.0f : 0.0f;
-  __syncthreads();   // sL complete
-  if (br == 0) {
-    const float inv0 = 1.0f / sL[0][0];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      x[0][c] *= inv0;
-      colbuf[0][c0 + c] = x[0][c];
-    }
-  }
-  __syncthreads();
-  for (int kb = 0; kb < NB / 8; ++kb) {
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = 8 * kb + kk;
-      const int buf = kk & 1;
-      if (wave_last_row > k) {
-        float m[8], xr[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) m[r] = (r0 + r > k) ? sL[r0 + r][k] : 0.0f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) xr[c] = colbuf[buf][c0 + c];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) x[r][c] = fmaf(-m[r], xr[c], x[r][c]);
-      }
-      // row k + 1 is now final up to its diagonal scale: its owners scale and publish it
-      const int kn = k + 1;
-      if (kn < NB && br == (kn >> 3)) {
-        const float inv = 1.0f / sL[kn][kn];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          x[(kk + 1) & 7][c] *= inv;
-          colbuf[buf ^ 1][c0 + c] = x[(kk + 1) & 7][c];
-        }
-      }
-      __syncthreads();
-    }
-  }
-  float* Xe = Linv + static_cast<int64_t>(e) * d_in * d_in + static_cast<int64_t>(k0) * d_in + k0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float4* dst = reinterpret_cast<float4*>(Xe + static_cast<int64_t>(r0 + r) * d_in + c0);
-    dst[0] = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
-    dst[1] = make_float4(x[r][4], x[r][5], x[r][6], x[r][7]);
+  leaf_node<NB>(sA, sX, 0, wave, lane, &bad);
+  if (t == 0 && bad) flag[e] = 1;
+  float* Le = Lbuf + e * bsl + static_cast<int64_t>(k0) * d_in + k0;
+  float* Xe = Linv + e * dd + static_cast<int64_t>(k0) * d_in + k0;
+#pragma unroll 4
+  for (int m = 0; m < NB / 8; ++m) {
+    const int row = t / 32 + 8 * m, c = 4 * (t % 32);
+    const float4 l = *reinterpret_cast<const float4*>(sA + row * LLD + c);
+    const float4 x = *reinterpret_cast<const float4*>(sX + row * LLD + c);
+    *reinterpret_cast<float4*>(Le + static_cast<int64_t>(row) * d_in + c) =
+        make_float4(c <= row ? l.x : 0.0f, c + 1 <= row ? l.y : 0.0f, c + 2 <= row ? l.z : 0.0f,
+                    c + 3 <= row ? l.w : 0.0f);
+    *reinterpret_cast<float4*>(Xe + static_cast<int64_t>(row) * d_in + c) =
+        make_float4(c <= row ? x.x : 0.0f, c + 1 <= row ? x.y : 0.0f, c + 2 <= row ? x.z : 0.0f,
+                    c + 3 <= row ? x.w : 0.0f);
   }
 }
 
@@ -375,7 +433,6 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
   if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_ERR_WORKSPACE;
   const dim3 blk(256);
   const int cb = (d_in + 255) / 256;
-  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
   GPTQ_LAUNCH(keys_kernel, dim3(cb, batch), blk, 0, stream, diag_key, d_in, w.key, dead, w.rank);
   if (p.act_order) {
     GPTQ_LAUNCH(actorder_rank_kernel, dim3(cb, (d_in + RANK_SLICE - 1) / RANK_SLICE, batch), blk, 0, stream, w.key,
