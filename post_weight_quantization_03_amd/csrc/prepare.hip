@@ -142,31 +142,46 @@ __device__ __forceinline__ float bcast_lane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// acc += sum over k in [k0, k1) of A(i0 + i, k) * B(k, j0 + j) for a 16x16 tile, with
-// A(i, k) = pa[i * LLD + k] and B(k, j) = pb[j * LLD + k] (kBT) or pb[k * LLD + j].
-// The K range (a multiple of 16) is split in four contiguous quarters, one per k-slot of
-// the 16x16x4 instruction, so each lane reads its A (and B^T) values 4 at a time.
+// acc += sum over k in [k0, k0 + 16 KS) of A(i0 + i, k) * B(k, j0 + j) for a 16x16 tile,
+// with A(i, k) = pa[i * LLD + k] and B(k, j) = pb[j * LLD + k] (kBT) or pb[k * LLD + j].
+// The K range is split in four contiguous quarters, one per k-slot of the 16x16x4
+// instruction, so each lane reads its A (and B^T) values 4 at a time; all reads are issued
+// before the first product.
+template <bool kBT, int KS>
+__device__ __forceinline__ f32x4v tile_mma_n(f32x4v acc, const float* pa, const float* pb, int k0, int lane) {
+  const int q = lane >> 4, rc = lane & 15;
+  const float* ar = pa + rc * LLD + k0 + q * 4 * KS;
+  const float* br = kBT ? pb + rc * LLD + k0 + q * 4 * KS : pb + (k0 + q * 4 * KS) * LLD + rc;
+  float4 av[KS], bv[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    av[s] = *reinterpret_cast<const float4*>(ar + 4 * s);
+    if (kBT) {
+      bv[s] = *reinterpret_cast<const float4*>(br + 4 * s);
+    } else {
+      bv[s] = make_float4(br[(4 * s) * LLD], br[(4 * s + 1) * LLD], br[(4 * s + 2) * LLD], br[(4 * s + 3) * LLD]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s].x, bv[s].x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s].y, bv[s].y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s].z, bv[s].z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s].w, bv[s].w, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Same over [k0, k1), k1 - k0 a multiple of 16 up to 64.
 template <bool kBT>
 __device__ __forceinline__ f32x4v tile_mma(f32x4v acc, const float* pa, const float* pb, int k0, int k1,
                                            int lane) {
-  const int kq = (k1 - k0) >> 2;
-  const int q = lane >> 4, rc = lane & 15;
-  const float* ar = pa + rc * LLD + k0 + q * kq;
-  const float* br = kBT ? pb + rc * LLD + k0 + q * kq : pb + (k0 + q * kq) * LLD + rc;
-  for (int s = 0; s < kq; s += 4) {
-    const float4 av = *reinterpret_cast<const float4*>(ar + s);
-    float4 bv;
-    if (kBT) {
-      bv = *reinterpret_cast<const float4*>(br + s);
-    } else {
-      bv = make_float4(br[s * LLD], br[(s + 1) * LLD], br[(s + 2) * LLD], br[(s + 3) * LLD]);
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
+  switch ((k1 - k0) >> 4) {
+    case 1: return tile_mma_n<kBT, 1>(acc, pa, pb, k0, lane);
+    case 2: return tile_mma_n<kBT, 2>(acc, pa, pb, k0, lane);
+    case 3: return tile_mma_n<kBT, 3>(acc, pa, pb, k0, lane);
+    default: return tile_mma_n<kBT, 4>(acc, pa, pb, k0, lane);
   }
-  return acc;
 }
 
 // 16x16 tile (rows 4*(lane/16) + r, column lane%16) of a result, to or from LDS.
@@ -181,77 +196,90 @@ __device__ __forceinline__ f32x4v tile_load(const float* p, int lane) {
   return v;
 }
 
-// Cholesky and inverse of the 16x16 diagonal block at (o, o), by the calling wave.
-// Lane i < 16 holds row i.  Column k: pivot d = a_kk (from lane k), l_ik = a_ik / sqrt(d),
-// then a_ij -= l_ik l_jk for j > k.  The inverse is formed column per lane: lane j solves
-// L x = e_j by forward substitution with the rows of L read out of lanes 0..15.
+// Cholesky and inverse of the 16x16 diagonal block at (o, o), by the calling wave, and,
+// when kPanel, the solve L21 = A21 L11^-T of the 16 rows below it (rows o+16..o+31).
+// Column k of the Cholesky takes pivot d = a_kk, scales l_rk = a_rk / sqrt(d) and then
+// a_rj -= l_rk l_jk for every later column j; forward substitution of L X = I takes
+// x_k /= l_kk and x_j -= l_jk x_k; the panel rows follow the Cholesky rows.  All three are
+// v_j -= v_k l_jk after v_k is scaled, so one register file v[] serves them:
+//   lanes  0..15: row r of the diagonal block,
+//   lanes 16..31: column r of X = L^-1 (starts as e_r),
+//   lanes 32..47: row r of the panel (kPanel).
+// The broadcast l_jk comes out of lane j by readlane; no barrier is needed.
+template <bool kPanel>
 __device__ __forceinline__ void leaf16(float* sA, float* sX, int o, int lane, int* bad) {
-  float a[16];
-  const int r = lane & 15;
-  const float* src = sA + (o + r) * LLD + o;
+  float v[16];
+  const int r = lane & 15, part = lane >> 4;
+  if (part == 1) {
 #pragma unroll
-  for (int c = 0; c < 16; c += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(src + c);
-    a[c] = v.x; a[c + 1] = v.y; a[c + 2] = v.z; a[c + 3] = v.w;
+    for (int i = 0; i < 16; ++i) v[i] = (r == i) ? 1.0f : 0.0f;
+  } else {
+    const int row = o + r + ((kPanel && part >= 2) ? 16 : 0);
+    const float* src = sA + row * LLD + o;
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+      const float4 u = *reinterpret_cast<const float4*>(src + c);
+      v[c] = u.x; v[c + 1] = u.y; v[c + 2] = u.z; v[c + 3] = u.w;
+    }
   }
-  float inv_l[16];
   bool ok = true;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const float d = bcast_lane(a[k], k);
+    const float d = bcast_lane(v[k], k);
     ok = ok && (d > 0.0f) && (d < INFINITY);
-    const float sq = sqrtf(d);
-    inv_l[k] = 1.0f / sq;
-    a[k] = (r == k) ? sq : a[k] * inv_l[k];
+    // 1/sqrt(d) by the hardware reciprocal square root (1 ulp); l_kk = d / sqrt(d)
+    const float il = __builtin_amdgcn_rsqf(d);
+    v[k] = (lane == k) ? d * il : v[k] * il;
 #pragma unroll
-    for (int j = k + 1; j < 16; ++j) a[j] = fmaf(-a[k], bcast_lane(a[k], j), a[j]);
+    for (int j = k + 1; j < 16; ++j) v[j] = fmaf(-v[k], bcast_lane(v[k], j), v[j]);
   }
   if (!ok) *bad = 1;
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float acc = (r == i) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int k = 0; k < i; ++k) acc = fmaf(-bcast_lane(a[k], i), x[k], acc);
-    x[i] = acc * inv_l[i];
-  }
-  if (lane < 16) {
+  if (part == 0) {
     float* dl = sA + (o + r) * LLD + o;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) dl[c] = (c <= r) ? a[c] : 0.0f;
+    for (int c = 0; c < 16; ++c) dl[c] = (c <= r) ? v[c] : 0.0f;
+  } else if (part == 1) {
     float* dx = sX + o * LLD + o + r;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dx[i * LLD] = x[i];
+    for (int i = 0; i < 16; ++i) dx[i * LLD] = v[i];
+  } else if (kPanel && part == 2) {
+    float* dl = sA + (o + 16 + r) * LLD + o;
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) *reinterpret_cast<float4*>(dl + c) = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
   }
 }
 
-template <int S>
+// kFirst: the node is the first half of its parent, and for S == 16 the leaf also solves
+// the parent's 16 panel rows (so a node of 32 needs no product for its L21).
+template <int S, bool kFirst>
 __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave, int lane, int* bad) {
   if constexpr (S == 16) {
-    if (wave == 0) leaf16(sA, sX, o, lane, bad);
+    if (wave == 0) leaf16<kFirst>(sA, sX, o, lane, bad);
     __syncthreads();
   } else {
     constexpr int H = S / 2, NT = H / 16, NTT = NT * NT, PER = (NTT + 3) / 4;
-    leaf_node<H>(sA, sX, o, wave, lane, bad);
+    leaf_node<H, true>(sA, sX, o, wave, lane, bad);
     const f32x4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    // L21 = A21 X11^T (X11 lower: k < 16 (tj + 1)), in place over A21
     f32x4v res[PER];
+    if constexpr (H > 16) {
+      // L21 = A21 X11^T (X11 lower: k < 16 (tj + 1)), in place over A21
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int t = wave + 4 * u;
-      if (t < NTT) {
-        const int ti = t / NT, tj = t % NT;
-        res[u] = tile_mma<true>(zero, sA + (o + H + 16 * ti) * LLD + o, sX + (o + 16 * tj) * LLD + o, 0,
-                                16 * (tj + 1), lane);
+      for (int u = 0; u < PER; ++u) {
+        const int t = wave + 4 * u;
+        if (t < NTT) {
+          const int ti = t / NT, tj = t % NT;
+          res[u] = tile_mma<true>(zero, sA + (o + H + 16 * ti) * LLD + o, sX + (o + 16 * tj) * LLD + o, 0,
+                                  16 * (tj + 1), lane);
+        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int t = wave + 4 * u;
-      if (t < NTT) tile_store(sA + (o + H + 16 * (t / NT)) * LLD + o + 16 * (t % NT), res[u], lane);
+      for (int u = 0; u < PER; ++u) {
+        const int t = wave + 4 * u;
+        if (t < NTT) tile_store(sA + (o + H + 16 * (t / NT)) * LLD + o + 16 * (t % NT), res[u], lane);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // S22 = A22 - L21 L21^T (lower tiles) and T = L21 X11 (X11 lower: k >= 16 tj) into X21
     constexpr int NLOW = NT * (NT + 1) / 2;
     for (int t = wave; t < NLOW + NTT; t += 4) {
@@ -271,7 +299,7 @@ __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave,
       }
     }
     __syncthreads();
-    leaf_node<H>(sA, sX, o + H, wave, lane, bad);
+    leaf_node<H, false>(sA, sX, o + H, wave, lane, bad);
     // X21 = -X22 T (X22 lower: k < 16 (ti + 1)), in place over T
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -311,7 +339,7 @@ __global__ __launch_bounds__(256) void potrf_block_kernel(const float* __restric
         *reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(row) * d_in + 4 * c4);
   }
   __syncthreads();
-  leaf_node<NB>(sA, sX, 0, wave, lane, &bad);
+  leaf_node<NB, false>(sA, sX, 0, wave, lane, &bad);
   if (t == 0 && bad) flag[e] = 1;
   float* Le = Lbuf + e * bsl + static_cast<int64_t>(k0) * d_in + k0;
   float* Xe = Linv + e * dd + static_cast<int64_t>(k0) * d_in + k0;
