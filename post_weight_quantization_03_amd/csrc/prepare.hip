@@ -17,6 +17,7 @@
 // kernel); everything else is fp32 matrix-core products.  A non-positive or non-finite pivot sets a device flag that
 // the host reads back (GPTQ_ERR_NOT_SPD).
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -369,6 +370,19 @@ __global__ __launch_bounds__(256) void reverse_to_upper_kernel(const float* __re
   U[static_cast<int64_t>(e) * bsu + static_cast<int64_t>(i) * d_in + j] = v;
 }
 
+// T = L21 L11^-1 of a node at recursion depth t lives at t_offset(t) of the T workspace:
+// one buffer per depth, because the T of a node is produced on the side stream while its
+// second half (deeper nodes) runs.  A node at depth t spans at most ceil(nb / 2^t) blocks.
+size_t t_offset(int depth, int nb, int batch) {
+  size_t off = 0;
+  for (int t = 0, span = nb; t < depth && span > 1; ++t) {
+    const size_t h2 = static_cast<size_t>((span + 1) / 2) * NB;
+    off += static_cast<size_t>(batch) * h2 * h2;
+    span = (span + 1) / 2;
+  }
+  return off;
+}
+
 struct PrepWs {
   double* key;
   int32_t* rank;
@@ -390,9 +404,34 @@ PrepWs carve(void* ws, int batch, int d_in) {
   w.flag = cv.take<int>(batch);
   w.A = cv.take<float>(batch * dd);
   w.Linv = cv.take<float>(batch * dd);
-  w.T = cv.take<float>(batch * dd / 4 + static_cast<size_t>(NB) * d_in);
+  w.T = cv.take<float>(t_offset(64, d_in / NB, batch));
   w.bytes = cv.used;
   return w;
+}
+
+// A second stream per device takes the products that are off the critical path of the
+// recursion; two events fork work onto it and join it back.  Created on first use, kept
+// for the life of the process.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+gptq_status side_stream(SideStream** out) {
+  int dev = 0;
+  GPTQ_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return GPTQ_ERR_HIP;
+  SideStream& ss = g_side[dev];
+  if (ss.s == nullptr) {
+    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
+    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+  }
+  *out = &ss;
+  return GPTQ_OK;
 }
 
 // Recursive Cholesky with the inverse, over the block range [b0, b1) of A (in place):
@@ -404,16 +443,29 @@ PrepWs carve(void* ws, int batch, int d_in) {
 // Leaves are single 128-column blocks (potrf_block_kernel).  Every product runs on the
 // fp32 matrix cores with triangular operands trimming the K range; most of the flops land
 // in the large products near the top of the recursion.
-gptq_status chol_inv(int b0, int b1, int batch, int d_in, float* A, float* L, int64_t bsl, float* Linv, float* T,
-                     int* flag, hipStream_t stream) {
+//
+// The chain leaf -> L21 -> S -> leaf ... is serial and mostly leaves the GPU idle, so
+// T = L21 L11^-1, needed only by the node's last product, runs on the side stream while
+// the second half recurses; the main stream waits for it just before that product.
+struct Sched {
+  hipStream_t main;
+  SideStream* side;
+  int nb, batch;
+};
+
+gptq_status chol_inv(int b0, int b1, int depth, int d_in, float* A, float* L, int64_t bsl, float* Linv,
+                     float* Tbase, int* flag, const Sched& sc) {
+  const int batch = sc.batch;
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  hipStream_t stream = sc.main;
   if (b1 - b0 == 1) {
     GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, stream, A, L, bsl, Linv, d_in, b0 * NB, flag);
     return GPTQ_OK;
   }
   const int bm = b0 + (b1 - b0) / 2;
   const int o1 = b0 * NB, o2 = bm * NB, h1 = (bm - b0) * NB, h2 = (b1 - bm) * NB;
-  gptq_status st = chol_inv(b0, bm, batch, d_in, A, L, bsl, Linv, T, flag, stream);
+  float* T = Tbase + t_offset(depth, sc.nb, batch);
+  gptq_status st = chol_inv(b0, bm, depth + 1, d_in, A, L, bsl, Linv, Tbase, flag, sc);
   if (st != GPTQ_OK) return st;
   GemmArgs g{};
   // L21 = A21 * (L11^-1)^T
@@ -423,6 +475,16 @@ gptq_status chol_inv(int b0, int b1, int batch, int d_in, float* A, float* L, in
   g.C = L + static_cast<int64_t>(o2) * d_in + o1; g.ldc = d_in; g.sC = bsl;
   g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower; g.batch = batch;
   if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
+  // T = L21 * L11^-1 on the side stream (L11^-1 lower: the K range of an output column starts at it)
+  GPTQ_HIP_TRY(hipEventRecord(sc.side->fork, stream));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(sc.side->s, sc.side->fork, 0));
+  GemmArgs t = g;
+  t.M = h2; t.N = h1; t.K = h1;
+  t.A = L + static_cast<int64_t>(o2) * d_in + o1; t.lda = d_in; t.sA = bsl;
+  t.B = Linv + static_cast<int64_t>(o1) * d_in + o1; t.ldb = d_in; t.sB = dd;
+  t.C = T; t.ldc = h1; t.sC = static_cast<int64_t>(h2) * h1;
+  t.alpha = 1.0f; t.beta = 0.0f; t.transB = 0; t.flags = kBLower;
+  if ((st = gemm_f32(t, sc.side->s)) != GPTQ_OK) return st;
   // S = A22 - L21 L21^T (lower tiles)
   g.M = h2; g.N = h2; g.K = h1;
   g.A = L + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = bsl;
@@ -430,14 +492,10 @@ gptq_status chol_inv(int b0, int b1, int batch, int d_in, float* A, float* L, in
   g.C = A + static_cast<int64_t>(o2) * d_in + o2; g.ldc = d_in; g.sC = dd;
   g.alpha = -1.0f; g.beta = 1.0f; g.transB = 1; g.flags = kLowerOut;
   if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
-  if ((st = chol_inv(bm, b1, batch, d_in, A, L, bsl, Linv, T, flag, stream)) != GPTQ_OK) return st;
-  // T = L21 * L11^-1   (L11^-1 lower: the K range of an output column starts at it)
-  g.M = h2; g.N = h1; g.K = h1;
-  g.A = L + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = bsl;
-  g.B = Linv + static_cast<int64_t>(o1) * d_in + o1; g.ldb = d_in; g.sB = dd;
-  g.C = T; g.ldc = h1; g.sC = static_cast<int64_t>(h2) * h1;
-  g.alpha = 1.0f; g.beta = 0.0f; g.transB = 0; g.flags = kBLower;
-  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
+  if ((st = chol_inv(bm, b1, depth + 1, d_in, A, L, bsl, Linv, Tbase, flag, sc)) != GPTQ_OK) return st;
+  // join: the side stream is in order, so its latest point covers this node's T
+  GPTQ_HIP_TRY(hipEventRecord(sc.side->join, sc.side->s));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(stream, sc.side->join, 0));
   // Linv21 = -L22^-1 * T   (L22^-1 lower: the K range of an output row ends at it)
   g.M = h2; g.N = h1; g.K = h2;
   g.A = Linv + static_cast<int64_t>(o2) * d_in + o2; g.lda = d_in; g.sA = dd;
@@ -472,8 +530,14 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
   GPTQ_LAUNCH(gather_reversed_kernel, dim3(cb, d_in, batch), blk, 0, stream, H, bsh, perm, w.key,
               w.lambda, d_in, w.A);
   // L is built in the U buffer (same shape), then replaced by U at the end.
-  gptq_status st = chol_inv(0, d_in / NB, batch, d_in, w.A, U, bsu, w.Linv, w.T, w.flag, stream);
-  if (st != GPTQ_OK) return st;
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    Sched sc{stream, nullptr, d_in / NB, batch};
+    gptq_status st = side_stream(&sc.side);
+    if (st != GPTQ_OK) return st;
+    st = chol_inv(0, d_in / NB, 0, d_in, w.A, U, bsu, w.Linv, w.T, w.flag, sc);
+    if (st != GPTQ_OK) return st;
+  }
   GPTQ_LAUNCH(reverse_to_upper_kernel, dim3(cb, d_in, batch), blk, 0, stream, w.Linv, d_in, U, bsu);
 
   // read back the per-problem pivot flags
