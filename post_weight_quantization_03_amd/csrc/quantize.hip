@@ -11,14 +11,16 @@
 //                    processing order, dead columns zeroed                 (workspace)
 //   row_grid:        per-row grid only: min/max of each whole row -> scale, zero
 //   per block b of 128 columns:
-//     block_sweep:   one lane per row keeps the row's 128 block columns in registers;
-//                    every lane quantizes its own row, so the column recurrence needs no
-//                    cross-lane traffic.  U's diagonal block is wave-uniform and is read
-//                    through the scalar cache.  Outputs codes (processing order), the
-//                    group scale/zero, and the block's columns of Err.
+//     block_sweep:   16 lanes per row keep the row's 128 block columns in registers
+//                    (8 each); the column value is broadcast within the row by DPP and
+//                    quantized by all 16; U's diagonal block sits in LDS.  Outputs codes
+//                    (processing order), the group scale/zero, and the block's columns
+//                    of Err.
 //     lazy update:   hierarchical (see sweep_range): W_p[:, right] -= Err[:, left] @ U[left,
 //                    right] on the fp32 matrix cores, Err [d_out, d_in] in processing order.
 //   unpermute:       codes back to original column order; g_idx.
+#include <utility>
+
 #include "common.h"
 
 namespace gptq {
@@ -78,132 +80,89 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
   }
 }
 
-// One 128-column block of the sweep.  G = group size (a divisor of 128), or 0 for the
-// per-row grid already written by row_grid_kernel.  One lane = one row.
-template <int G>
-__global__ __launch_bounds__(64) void block_sweep_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
-                                                         int64_t bsu, int d_out, int d_in, int blk, float maxq,
-                                                         float* __restrict__ scales, uint8_t* __restrict__ zeros,
-                                                         uint8_t* __restrict__ codes_p, float* __restrict__ err) {
-  const int e = blockIdx.y;
-  const int r = blockIdx.x * 64 + threadIdx.x;
-  if (r >= d_out) return;
-  const int j0 = blk * kBlock;
-  const int n_groups = G ? d_in / G : 1;
-  float w[kBlock];
-  const float4* src = reinterpret_cast<const float4*>(Wp + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
-#pragma unroll
-  for (int i = 0; i < kBlock / 4; ++i) {
-    const float4 v = src[i];
-    w[4 * i] = v.x;
-    w[4 * i + 1] = v.y;
-    w[4 * i + 2] = v.z;
-    w[4 * i + 3] = v.w;
-  }
-  const float* Ub = U + static_cast<int64_t>(e) * bsu + static_cast<int64_t>(j0) * d_in + j0;
-  float* sc = scales + static_cast<int64_t>(e) * n_groups * d_out;
-  uint8_t* zr = zeros + static_cast<int64_t>(e) * n_groups * d_out;
-  float s = 1.0f, z = 0.0f, inv_s = 1.0f;
-  if constexpr (G == 0) {
-    s = sc[r];
-    z = static_cast<float>(zr[r]);
-    inv_s = 1.0f / s;
-  }
-  uint32_t cw[kBlock / 4];
-#pragma unroll
-  for (int i = 0; i < kBlock / 4; ++i) cw[i] = 0u;
-
-#pragma unroll
-  for (int j = 0; j < kBlock; ++j) {
-    if constexpr (G != 0) {
-      if (j % G == 0) {
-        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-          lo = fminf(lo, w[j + k]);
-          hi = fmaxf(hi, w[j + k]);
-        }
-        s = fmaxf((hi - lo) / maxq, 1e-8f);
-        z = rintf(-lo / s);
-        inv_s = 1.0f / s;
-        const int gi = (j0 + j) / G;
-        sc[static_cast<int64_t>(gi) * d_out + r] = s;
-        zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
-      }
-    }
-    const float q = fminf(fmaxf(rintf(w[j] * inv_s) + z, 0.0f), maxq);
-    const float wq = s * (q - z);
-    const float e_j = (w[j] - wq) * (1.0f / Ub[j * d_in + j]);
-    cw[j / 4] |= static_cast<uint32_t>(q) << (8 * (j % 4));
-#pragma unroll
-    for (int k = j + 1; k < kBlock; ++k) w[k] = fmaf(-e_j, Ub[j * d_in + k], w[k]);
-    w[j] = e_j;
-  }
-  uint4* cdst = reinterpret_cast<uint4*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
-#pragma unroll
-  for (int i = 0; i < kBlock / 16; ++i) cdst[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
-  float4* edst = reinterpret_cast<float4*>(err + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
-#pragma unroll
-  for (int i = 0; i < kBlock / 4; ++i) edst[i] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-}
-
-// Broadcast lane `src` of each group of four lanes (DPP quad_perm).
+// DPP within a row of 16 lanes: broadcast of lane `src`, and rotation by `n`.
 template <int src>
-__device__ __forceinline__ float quad_bcast(float v) {
-  constexpr int ctrl = src | (src << 2) | (src << 4) | (src << 6);
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + src, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float quad_min(float v) {
-  v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // [1,0,3,2]
-  return fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // [2,3,0,1]
+template <int n>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + n, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+__device__ __forceinline__ float row_min(float v) {
+  v = fminf(v, row_ror<8>(v));
+  v = fminf(v, row_ror<4>(v));
+  v = fminf(v, row_ror<2>(v));
+  return fminf(v, row_ror<1>(v));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
 }
 
-constexpr int QP = 36;   // LDS stride (floats) of one lane's 32 U values of a row
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
-// One 128-column block of the sweep with four lanes per row: lane k of a quad keeps
-// columns 4m + k (m = 0..31) of its row in registers.  For column j, the owner lane's
-// value is broadcast to the quad (DPP), every lane of the quad quantizes it (so all four
-// hold err_j and code_j), and each lane updates its own later columns.  The U block sits
-// in LDS as Ul[j][k][m] = U[j0 + j][j0 + 4m + k] with its diagonal zeroed (1/U_jj kept
-// apart), so a lane's update reads are contiguous and columns at or before j get a zero
-// factor.  A workgroup of 256 threads handles 64 rows.
+constexpr int SW_ROWS = 16;   // rows of W per workgroup: 16 lanes per row, 4 rows per wave
+
+// One 128-column block of the sweep.  G = group size (16, 32, 64 or 128), or 0 for the
+// per-row grid already written by row_grid_kernel.
+//
+// A row of W is spread over one DPP row of 16 lanes: lane k keeps columns 16m + k
+// (m = 0..7) in registers.  For column j the owner lane's value is broadcast to the row
+// (row_newbcast), every lane of the row quantizes it (so all 16 hold err_j and code_j),
+// and each lane updates its own later columns.  The U block sits in LDS as
+// Ul[j][8k + m] = U[j0 + j][j0 + 16m + k] with its diagonal zeroed (1/U_jj kept apart):
+// a lane's update reads are contiguous, the four rows of a wave read the same words, and
+// columns at or before j get a zero factor.  At a group start the grid is fitted on the
+// row's current values of the group's columns (min/max reduced over the 16 lanes).
 template <int G>
-__global__ __launch_bounds__(256) void block_sweep_quad_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
-                                                               int64_t bsu, int d_out, int d_in, int blk, float maxq,
-                                                               float* __restrict__ scales, uint8_t* __restrict__ zeros,
-                                                               uint8_t* __restrict__ codes_p, float* __restrict__ err) {
-  __shared__ __attribute__((aligned(16))) float Ul[kBlock][4][QP];
+__global__ __launch_bounds__(256) void block_sweep_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
+                                                          int64_t bsu, int d_out, int d_in, int blk, float maxq,
+                                                          float* __restrict__ scales, uint8_t* __restrict__ zeros,
+                                                          uint8_t* __restrict__ codes_p, float* __restrict__ err) {
+  __shared__ __attribute__((aligned(16))) float Ul[kBlock * kBlock];
   __shared__ float inv_d[kBlock];
   const int e = blockIdx.y;
   const int tid = threadIdx.x;
   const int j0 = blk * kBlock;
   const float* Ub = U + static_cast<int64_t>(e) * bsu + static_cast<int64_t>(j0) * d_in + j0;
-  // stage the U block: thread handles float4 chunks (row j, columns 4m..4m+3)
-  for (int i = tid; i < kBlock * kBlock / 4; i += 256) {
-    const int j = i >> 5, m = i & 31;
-    const float4 v = *reinterpret_cast<const float4*>(Ub + static_cast<int64_t>(j) * d_in + 4 * m);
-    Ul[j][0][m] = (4 * m + 0 == j) ? 0.0f : v.x;
-    Ul[j][1][m] = (4 * m + 1 == j) ? 0.0f : v.y;
-    Ul[j][2][m] = (4 * m + 2 == j) ? 0.0f : v.z;
-    Ul[j][3][m] = (4 * m + 3 == j) ? 0.0f : v.w;
-    if (4 * m <= j && j < 4 * m + 4) {
-      const float dj = (j == 4 * m) ? v.x : (j == 4 * m + 1) ? v.y : (j == 4 * m + 2) ? v.z : v.w;
-      inv_d[j] = 1.0f / dj;
+  const int r = blockIdx.x * SW_ROWS + (tid >> 4);
+  const int k = tid & 15;
+  const bool live = r < d_out;
+  // the row's block columns are fetched first, so they arrive while U is staged
+  const float* wrow = Wp + (static_cast<int64_t>(e) * d_out + (live ? r : 0)) * d_in + j0;
+  float w[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) w[m] = wrow[16 * m + k];
+  // stage the U block: thread (row j, lane kk) gathers U[j][16m + kk], m = 0..7 (each load
+  // instruction reads 16 consecutive floats across the lanes) and writes them as 8
+  // consecutive floats
+#pragma unroll 2
+  for (int i = tid; i < kBlock * 16; i += 256) {
+    const int j = i >> 4, kk = i & 15;
+    const float* src = Ub + static_cast<int64_t>(j) * d_in + kk;
+    float v[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = src[16 * m];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (16 * m + kk == j) {
+        inv_d[j] = 1.0f / v[m];
+        v[m] = 0.0f;
+      }
     }
+    float4* dst = reinterpret_cast<float4*>(Ul + j * kBlock + 8 * kk);
+    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
   __syncthreads();
-  const int r = blockIdx.x * 64 + (tid >> 2);
-  const int k = tid & 3;
-  if (r >= d_out) return;
+  if (!live) return;   // whole rows of 16 lanes leave together; no barrier follows
   const int n_groups = G ? d_in / G : 1;
-  const float* wrow = Wp + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
-  float w[32];
-#pragma unroll
-  for (int m = 0; m < 32; ++m) w[m] = wrow[4 * m + k];
   float* sc = scales + static_cast<int64_t>(e) * n_groups * d_out;
   uint8_t* zr = zeros + static_cast<int64_t>(e) * n_groups * d_out;
   float s = 1.0f, z = 0.0f, inv_s = 1.0f;
@@ -212,61 +171,67 @@ __global__ __launch_bounds__(256) void block_sweep_quad_kernel(const float* __re
     z = static_cast<float>(zr[r]);
     inv_s = 1.0f / s;
   }
-  uint32_t cw[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) cw[i] = 0u;
-  const float* ul_k = &Ul[0][k][0];
+  // lane k stores the codes of columns 8k..8k+7 (two words)
+  uint32_t cw0 = 0u, cw1 = 0u;
+  const float* ul_k = Ul + 8 * k;
+  // U row j is read into registers one column ahead (two alternating sets), so that the
+  // LDS latency stays off the column-to-column chain
+  float4 ua0 = *reinterpret_cast<const float4*>(ul_k), ua1 = *reinterpret_cast<const float4*>(ul_k + 4);
+  float4 ub0, ub1;
+  float dja = inv_d[0], djb = 0.0f;
 
+  static_for(std::make_integer_sequence<int, kBlock>{}, [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int mj = j >> 4;
+    float4& cur0 = (j & 1) ? ub0 : ua0;
+    float4& cur1 = (j & 1) ? ub1 : ua1;
+    float4& nxt0 = (j & 1) ? ua0 : ub0;
+    float4& nxt1 = (j & 1) ? ua1 : ub1;
+    const float dj = (j & 1) ? djb : dja;
+    if constexpr (j + 1 < kBlock) {
+      const float* un = ul_k + (j + 1) * kBlock;
+      if constexpr (((j + 1) >> 4) < 4) nxt0 = *reinterpret_cast<const float4*>(un);
+      nxt1 = *reinterpret_cast<const float4*>(un + 4);
+      if constexpr (j & 1) dja = inv_d[j + 1];
+      else djb = inv_d[j + 1];
+      // the scheduler would sink these reads next to their use in the next column
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (G != 0 && j % G == 0) {
+      float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kBlock; ++j) {
-    const int mj = j >> 2;
-    if constexpr (G != 0) {
-      if (j % G == 0) {
-        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-        for (int m = j / 4; m < (j + G) / 4; ++m) {
-          lo = fminf(lo, w[m]);
-          hi = fmaxf(hi, w[m]);
-        }
-        lo = quad_min(lo);
-        hi = quad_max(hi);
-        s = fmaxf((hi - lo) / maxq, 1e-8f);
-        z = rintf(-lo / s);
-        inv_s = 1.0f / s;
-        if (k == 0) {
-          const int gi = (j0 + j) / G;
-          sc[static_cast<int64_t>(gi) * d_out + r] = s;
-          zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
-        }
+      for (int m = j / 16; m < (j + G) / 16; ++m) {
+        lo = fminf(lo, w[m]);
+        hi = fmaxf(hi, w[m]);
+      }
+      lo = row_min(lo);
+      hi = row_max(hi);
+      s = fmaxf((hi - lo) / maxq, 1e-8f);
+      z = rintf(-lo / s);
+      inv_s = 1.0f / s;
+      if (k == 0) {
+        const int gi = (j0 + j) / G;
+        sc[static_cast<int64_t>(gi) * d_out + r] = s;
+        zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
       }
     }
-    float wj;
-    switch (j & 3) {
-      case 0: wj = quad_bcast<0>(w[mj]); break;
-      case 1: wj = quad_bcast<1>(w[mj]); break;
-      case 2: wj = quad_bcast<2>(w[mj]); break;
-      default: wj = quad_bcast<3>(w[mj]); break;
-    }
+    const float wj = row_bcast<j & 15>(w[mj]);
     const float q = fminf(fmaxf(rintf(wj * inv_s) + z, 0.0f), maxq);
     const float wq = s * (q - z);
-    const float e_j = (wj - wq) * inv_d[j];
-    cw[j >> 2] |= static_cast<uint32_t>(q) << (8 * (j & 3));
-    // update this lane's columns 4m + k > j (the LDS factor is zero for columns <= j)
-    const float* urow = ul_k + j * (4 * QP);
+    const float e_j = (wj - wq) * dj;
+    const uint32_t qb = (k == (j >> 3)) ? (static_cast<uint32_t>(q) << (8 * (j & 3))) : 0u;
+    if constexpr ((j & 4) == 0) cw0 |= qb;
+    else cw1 |= qb;
+    const float u[8] = {cur0.x, cur0.y, cur0.z, cur0.w, cur1.x, cur1.y, cur1.z, cur1.w};
 #pragma unroll
-    for (int m = mj; m < 32; ++m) w[m] = fmaf(-e_j, urow[m], w[m]);
-    if (k == (j & 3)) w[mj] = e_j;   // the owner keeps err_j in place of w_j
-  }
-  // codes: every lane holds all 128; lane k stores words [8k, 8k+8)
-  uint32_t* cdst = reinterpret_cast<uint32_t*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
-  // lane-dependent word choice by masks (keeps cw[] in registers; no dynamic indexing)
-  const uint32_t m0 = k == 0 ? ~0u : 0u, m1 = k == 1 ? ~0u : 0u, m2 = k == 2 ? ~0u : 0u, m3 = k == 3 ? ~0u : 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    cdst[8 * k + i] = (cw[i] & m0) | (cw[8 + i] & m1) | (cw[16 + i] & m2) | (cw[24 + i] & m3);
+    for (int m = mj; m < 8; ++m) w[m] = fmaf(-e_j, u[m], w[m]);
+    if (k == (j & 15)) w[mj] = e_j;   // the owner keeps err_j in place of w_j
+  });
+  uint2* cdst = reinterpret_cast<uint2*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
+  cdst[k] = make_uint2(cw0, cw1);
   float* edst = err + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
 #pragma unroll
-  for (int m = 0; m < 32; ++m) edst[4 * m + k] = w[m];
+  for (int m = 0; m < 8; ++m) edst[16 * m + k] = w[m];
 }
 
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p,
@@ -307,7 +272,7 @@ template <int G>
 gptq_status launch_sweep(dim3 grid, hipStream_t stream, const float* Wp, const float* U, int64_t bsu, int d_out,
                          int d_in, int blk, float maxq, float* scales, uint8_t* zeros, uint8_t* codes_p,
                          float* err) {
-  GPTQ_LAUNCH(block_sweep_quad_kernel<G>, grid, dim3(256), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales,
+  GPTQ_LAUNCH(block_sweep_kernel<G>, grid, dim3(256), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales,
               zeros, codes_p, err);
   return GPTQ_OK;
 }
@@ -383,7 +348,7 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
   if (G == 0) {
     GPTQ_LAUNCH(row_grid_kernel, dim3(d_out, batch), blk, 0, stream, w.Wp, d_out, d_in, maxq, scales, zeros);
   }
-  const dim3 sg((d_out + 63) / 64, batch);
+  const dim3 sg((d_out + SW_ROWS - 1) / SW_ROWS, batch);
   const gptq_status st = sweep_range(0, d_in / kBlock, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales,
                                      zeros);
   if (st != GPTQ_OK) return st;
