@@ -182,9 +182,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return GPTQ_OK;
-  // 128-wide tiles when they alone give every CU at least two workgroups, else 64-wide
+  // 128-wide tiles when they give every CU two workgroups, or one for a plain product
+  // (triangular operands leave some tiles with far less work, a lower-only output skips
+  // half of them); else 64-wide
   const int64_t tiles128 = static_cast<int64_t>((g.N + 127) / 128) * ((g.M + 127) / 128) * g.batch;
-  const bool big = tiles128 >= 512;
+  const bool big = tiles128 >= 512 || (g.flags == 0 && tiles128 >= 256);
   const int T = big ? 128 : 64;
   const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, g.batch);
   if (big) {
