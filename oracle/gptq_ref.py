@@ -48,7 +48,8 @@ import numpy as np
 from scipy.linalg import solve_triangular
 
 __all__ = [
-    "NotSPD", "widen", "ref_accumulate_hessian", "ref_prepare_hinv", "fit_minmax",
+    "NotSPD", "widen", "ref_accumulate_hessian", "ref_channel_energy", "ref_hessian_entries",
+    "ref_column_order", "ref_prepare_hinv", "fit_minmax",
     "gptq_sweep", "MinMaxGrid", "ref_quantize_layer", "ref_dequantize",
     "ref_layer_loss", "ref_pack_int4", "ref_unpack_int4", "ref_gptq_layer",
 ]
@@ -90,7 +91,44 @@ def ref_accumulate_hessian(X: np.ndarray, dtype: str, H: np.ndarray | None = Non
     return H, n_seen + n
 
 
+def ref_channel_energy(X: np.ndarray, dtype: str, rows_per_step: int = 8192) -> np.ndarray:
+    """The diagonal of ref_accumulate_hessian alone: 2 * sum_t x_ti^2 per channel i, in
+    fp64 and token order, a slab at a time (no d_in x d_in matrix is formed)."""
+    n, d = X.shape
+    e = np.zeros(d, dtype=np.float64)
+    for t0 in range(0, n, rows_per_step):
+        x = widen(X[t0:t0 + rows_per_step], dtype)
+        e += 2.0 * np.einsum("ti,ti->i", x, x)
+    return e
+
+
+def ref_hessian_entries(X: np.ndarray, dtype: str, rows: np.ndarray, cols: np.ndarray,
+                        rows_per_step: int = 8192) -> np.ndarray:
+    """The block H[rows][:, cols] of ref_accumulate_hessian alone, 2 * X[:, rows]^T X[:, cols]."""
+    n = X.shape[0]
+    B = np.zeros((len(rows), len(cols)), dtype=np.float64)
+    for t0 in range(0, n, rows_per_step):
+        xr = widen(X[t0:t0 + rows_per_step][:, rows], dtype)
+        xc = widen(X[t0:t0 + rows_per_step][:, cols], dtype)
+        B += 2.0 * (xr.T @ xc)
+    return B
+
+
 # ----------------------------------------------- dead inputs, ActOrder, damping, U
+
+def ref_column_order(diag: np.ndarray, act_order: bool = False):
+    """Steps 1-2 of ref_prepare_hinv from the Hessian diagonal alone: (perm, dead, diag
+    with dead inputs set to 1).  [ARCH] "The algorithm in code" (dead inputs), [ACT] and
+    [SRS] 1.9 (descending diagonal; ties keep the original order)."""
+    diag = np.array(diag, dtype=np.float64, copy=True)
+    dead = diag == 0
+    diag[dead] = 1.0
+    if act_order:
+        perm = np.argsort(-diag, kind="stable")
+    else:
+        perm = np.arange(diag.shape[0])
+    return perm.astype(np.int64), dead, diag
+
 
 def ref_prepare_hinv(H: np.ndarray, damp: float = 0.01, act_order: bool = False):
     """From H to the upper Cholesky factor U of the damped, permuted H^-1.
@@ -106,14 +144,8 @@ def ref_prepare_hinv(H: np.ndarray, damp: float = 0.01, act_order: bool = False)
     """
     H = np.array(H, dtype=np.float64, copy=True)
     d = H.shape[0]
-    diag = np.diag(H).copy()
-    dead = diag == 0
-    diag[dead] = 1.0
+    perm, dead, diag = ref_column_order(np.diag(H), act_order)
     H[np.diag_indices(d)] = diag
-    if act_order:
-        perm = np.argsort(-diag, kind="stable")
-    else:
-        perm = np.arange(d)
     Hp = H[np.ix_(perm, perm)]
     lam = damp * float(np.mean(np.diag(Hp)))
     Hp[np.diag_indices(d)] += lam
@@ -129,7 +161,7 @@ def ref_prepare_hinv(H: np.ndarray, damp: float = 0.01, act_order: bool = False)
         U = np.linalg.cholesky(Hinv).T                   # upper: Hinv = U^T U
     except np.linalg.LinAlgError as exc:
         raise NotSPD(str(exc)) from None
-    return dict(U=U, perm=perm.astype(np.int64), dead=dead, lam=lam, Hp=Hp)
+    return dict(U=U, perm=perm, dead=dead, lam=lam, Hp=Hp)
 
 
 # --------------------------------------------------------------- grid ([ARCH] fit_group)

@@ -74,3 +74,13 @@ def test_generator_is_deterministic_and_chunkable():
     assert X1.shape == (300, 128) and X1.dtype == np.uint16
     s = synth.make_channel_scales(spec)
     assert np.array_equal(X1[128:256], synth.make_sequence(spec, 1, 128, s))
+
+
+def test_channel_energy_and_entry_blocks_match_brute_force_exactly():
+    # integer inputs: every product and sum is exact in fp64, so equality is exact
+    rng = np.random.default_rng(7)
+    X = rng.integers(-9, 10, size=(29, 7)).astype(np.float32)
+    Hb = brute_hessian(X.astype(int).tolist())
+    assert np.array_equal(R.ref_channel_energy(X, "f32", rows_per_step=4), np.diag(Hb))
+    rows, cols = np.array([6, 0, 3]), np.array([1, 1, 5, 2])
+    assert np.array_equal(R.ref_hessian_entries(X, "f32", rows, cols, rows_per_step=5), Hb[np.ix_(rows, cols)])

@@ -105,3 +105,14 @@ def test_reversed_factorisation_gives_the_same_U():
     L = np.linalg.cholesky(p["Hp"][np.ix_(J, J)])
     U2 = np.linalg.inv(L)[np.ix_(J, J)]
     np.testing.assert_allclose(U2, p["U"], rtol=1e-9, atol=1e-12)
+
+
+def test_column_order_from_the_diagonal_alone():
+    # dead inputs (zero diagonal) count as 1; descending; ties keep the original order
+    diag = np.array([2.0, 0.0, 5.0, 1.0, 2.0, 0.0, 7.0])
+    perm, dead, fixed = R.ref_column_order(diag, act_order=True)
+    assert perm.tolist() == [6, 2, 0, 4, 1, 3, 5]
+    assert dead.tolist() == [False, True, False, False, False, True, False]
+    assert fixed.tolist() == [2.0, 1.0, 5.0, 1.0, 2.0, 1.0, 7.0]
+    perm0, _, _ = R.ref_column_order(diag, act_order=False)
+    assert perm0.tolist() == list(range(7))
