@@ -94,12 +94,22 @@ def ref_accumulate_hessian(X: np.ndarray, dtype: str, H: np.ndarray | None = Non
 def ref_channel_energy(X: np.ndarray, dtype: str, rows_per_step: int = 8192) -> np.ndarray:
     """The diagonal of ref_accumulate_hessian alone: 2 * sum_t x_ti^2 per channel i, in
     fp64 and token order, a slab at a time (no d_in x d_in matrix is formed)."""
+    import torch   # plain CPU tensor ops: the same sums, spread over the host cores
+
     n, d = X.shape
-    e = np.zeros(d, dtype=np.float64)
+    e = torch.zeros(d, dtype=torch.float64)
     for t0 in range(0, n, rows_per_step):
-        x = widen(X[t0:t0 + rows_per_step], dtype)
-        e += 2.0 * np.einsum("ti,ti->i", x, x)
-    return e
+        slab = np.ascontiguousarray(X[t0:t0 + rows_per_step])
+        if dtype == "bf16":
+            # exact widening of the bf16 bits to fp32; a bf16 value has 8 significant bits,
+            # so its square is exact in fp32, and the sum runs in fp64
+            bits = torch.from_numpy(slab.view(np.int16)).to(torch.int32).bitwise_and(0xFFFF)
+            x = torch.bitwise_left_shift(bits, 16).view(torch.float32)
+            e += 2.0 * (x * x).sum(dim=0, dtype=torch.float64)
+        else:
+            x = torch.from_numpy(widen(slab, dtype))
+            e += 2.0 * (x * x).sum(dim=0)
+    return e.numpy()
 
 
 def ref_hessian_entries(X: np.ndarray, dtype: str, rows: np.ndarray, cols: np.ndarray,

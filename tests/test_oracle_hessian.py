@@ -84,3 +84,10 @@ def test_channel_energy_and_entry_blocks_match_brute_force_exactly():
     assert np.array_equal(R.ref_channel_energy(X, "f32", rows_per_step=4), np.diag(Hb))
     rows, cols = np.array([6, 0, 3]), np.array([1, 1, 5, 2])
     assert np.array_equal(R.ref_hessian_entries(X, "f32", rows, cols, rows_per_step=5), Hb[np.ix_(rows, cols)])
+
+
+def test_channel_energy_of_bf16_inputs_equals_the_hessian_diagonal():
+    spec = synth.scaled("attn_proj", d_out=8, d_in=64, n_tokens=3000, seq_len=1000)
+    X = synth.make_activations(spec, 0)
+    H, _ = R.ref_accumulate_hessian(X, "bf16", rows_per_step=700)
+    np.testing.assert_allclose(R.ref_channel_energy(X, "bf16", rows_per_step=500), np.diag(H), rtol=1e-14)
