@@ -314,8 +314,10 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
 }
 
 // Sums the token-slice partials of each lower tile in slice order and adds twice the
-// sum to H and to its mirror.  Block: 64x64 sub-block of one tile; mirror writes go
-// through LDS so both stores are coalesced.
+// sum to H and to its mirror.  Block: 64x64 sub-block of one tile, each thread 4 rows of
+// 4 consecutive columns (16-byte loads; the slice loop is unrolled so several slices'
+// loads are in flight, the additions keep slice order).  Mirror writes go through LDS so
+// both stores are coalesced.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ partial,
                                                           int nsplit, int ntiles, int d_in,
                                                           float* __restrict__ H, int64_t bsh) {
@@ -328,21 +330,37 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   lower_tile_coords(tile, I, J);
   const bool diag = (I == J);
   if (diag && sm < sn) return;  // strictly-upper sub-block of a diagonal tile
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int c4 = 4 * (threadIdx.x & 15), r0 = threadIdx.x >> 4;   // rows r0 + 16 q
   float* He = H + static_cast<int64_t>(e) * bsh;
   const int64_t tstride = static_cast<int64_t>(ST) * ST;
-  const float* P0 = partial + (static_cast<int64_t>(e) * nsplit * ntiles + tile) * tstride;
-  for (int i = ty; i < 64; i += 4) {
-    const int m = sm + i, n = sn + tx;
-    float s = 0.0f;
-    for (int k = 0; k < nsplit; ++k) s += P0[static_cast<int64_t>(k) * ntiles * tstride + m * ST + n];
-    const float v = 2.0f * s;
-    tr[i][tx] = v;
-    const int row = I * ST + m, col = J * ST + n;
-    if (row < d_in && col < d_in && (!diag || m >= n)) He[static_cast<int64_t>(row) * d_in + col] += v;
+  const int64_t kstride = static_cast<int64_t>(ntiles) * tstride;
+  const float* P0 = partial + (static_cast<int64_t>(e) * nsplit * ntiles + tile) * tstride + sm * ST + sn + c4;
+  float4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = 0; k < nsplit; ++k) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(P0 + k * kstride + (r0 + 16 * q) * ST);
+      acc[q].x += v.x; acc[q].y += v.y; acc[q].z += v.z; acc[q].w += v.w;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = r0 + 16 * q, m = sm + i;
+    const float v[4] = {2.0f * acc[q].x, 2.0f * acc[q].y, 2.0f * acc[q].z, 2.0f * acc[q].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = sn + c4 + t;
+      tr[i][c4 + t] = v[t];
+      const int row = I * ST + m, col = J * ST + n;
+      if (row < d_in && col < d_in && (!diag || m >= n)) He[static_cast<int64_t>(row) * d_in + col] += v[t];
+    }
   }
   __syncthreads();
   // mirror: H[col][row] for the same sub-block, written along rows of the transpose
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int i = ty; i < 64; i += 4) {
     const int n = sn + i, m = sm + tx;       // element (m, n) of the tile
     const int row = I * ST + m, col = J * ST + n;
@@ -463,7 +481,9 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
   pl.ksplit = 1;
   pl.kchunk = n_tokens;
   if (mfma) {
-    const int64_t want = (1024 + static_cast<int64_t>(pl.ntiles) * batch - 1) /
+    // about 2048 workgroups (8 per CU): shorter token slices balance the CUs better than
+    // the extra partial tiles cost in the reduction
+    const int64_t want = (2048 + static_cast<int64_t>(pl.ntiles) * batch - 1) /
                          (static_cast<int64_t>(pl.ntiles) * batch);
     const int64_t cap = std::max<int64_t>(1, n_tokens / kMinTokensPerSplit);
     pl.ksplit = static_cast<int>(std::min<int64_t>(std::min(want, cap), 64));
