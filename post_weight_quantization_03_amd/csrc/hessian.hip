@@ -49,13 +49,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes
-// land at LDS address lds_base + 16 l; lds_base must be wave-uniform.  Issued from inline
+// land at LDS byte address base + 16 l; base must be wave-uniform (a scalar register).  Issued from inline
 // assembly so that the compiler does not fence every later LDS read on it; the caller
 // waits for completion with s_waitcnt vmcnt.  m0 is saved and restored around the copy.
-__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
-  // the address is wave-uniform by contract; readfirstlane makes that visible to the compiler
-  const unsigned base = __builtin_amdgcn_readfirstlane(
-      static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(lds_dst))));
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned base) {
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -134,31 +131,51 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
   const bool full_cols = (I0 + ST <= d_in) && (J0 + ST <= d_in);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
   // Stage loader.  Fast path (all 32 rows and all 256 channels valid): each wave issues 2
   // direct global->LDS copies of 2 token rows (64 lanes x 16 bytes, lane-linear in LDS)
   // per operand; lane l fills physical chunk l%32 of its row, i.e. fetches logical chunk
-  // (l%32) ^ swizzle.  Tail stages go through registers with zero fill.
-  auto load_stage = [&](int64_t t0, int C0, uint16_t* dst) {
+  // (l%32) ^ swizzle.  The per-lane sources of stage 0 and the wave's LDS offsets are
+  // computed once; stage k adds k * SBK rows.  Tail stages go through registers with
+  // zero fill.
+  const int crow = 4 * wave + (lane >> 5);                 // + 2 for the second copy
+  const uint16_t* srcA0 = Xe + (t_begin + crow) * ldx + I0 + 8 * swz_chunk(crow, lane & 31);
+  const uint16_t* srcA1 = Xe + (t_begin + crow + 2) * ldx + I0 + 8 * swz_chunk(crow + 2, lane & 31);
+  const uint16_t* srcB0 = Xe + (t_begin + crow) * ldx + J0 + 8 * swz_chunk(crow, lane & 31);
+  const uint16_t* srcB1 = Xe + (t_begin + crow + 2) * ldx + J0 + 8 * swz_chunk(crow + 2, lane & 31);
+  constexpr unsigned kBufBytes = SBK * ST * 2, kRowBytes = ST * 2;
+  const unsigned ldsA = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(&sA[0][0]))) +
+                        4 * wave * kRowBytes;
+  const unsigned ldsB = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(&sB[0][0]))) +
+                        4 * wave * kRowBytes;
+  auto load_stage = [&](int k) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(k) * SBK;
+    const int buf = k % NBUF;
     const int rows = static_cast<int>(min<int64_t>(SBK, t_end - t0));
     if (rows == SBK && full_cols) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 4 * wave + 2 * i + (lane >> 5);
-        const int c = swz_chunk(r, lane & 31);
-        lds_dma16(Xe + (t0 + r) * ldx + C0 + 8 * c, dst + (4 * wave + 2 * i) * ST);
+      const int64_t off = static_cast<int64_t>(k) * SBK * ldx;
+      const unsigned lb = buf * kBufBytes;
+      lds_dma16(srcA0 + off, ldsA + lb);
+      lds_dma16(srcA1 + off, ldsA + lb + 2 * kRowBytes);
+      if (!diag) {
+        lds_dma16(srcB0 + off, ldsB + lb);
+        lds_dma16(srcB1 + off, ldsB + lb + 2 * kRowBytes);
       }
     } else {
+      for (int op = 0; op < (diag ? 1 : 2); ++op) {
+        const int C0 = op ? J0 : I0;
+        uint16_t* dst = op ? sB[buf] : sA[buf];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 4 * wave + 2 * i + (lane >> 5);
-        const int p = lane & 31;
-        const int c = swz_chunk(r, p);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < rows && C0 + 8 * c < d_in) v = *reinterpret_cast<const uint4*>(Xe + (t0 + r) * ldx + C0 + 8 * c);
-        *reinterpret_cast<uint4*>(dst + r * ST + 8 * p) = v;
+        for (int i = 0; i < 2; ++i) {
+          const int r = 4 * wave + 2 * i + (lane >> 5);
+          const int p = lane & 31;
+          const int c = swz_chunk(r, p);
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if (r < rows && C0 + 8 * c < d_in) v = *reinterpret_cast<const uint4*>(Xe + (t0 + r) * ldx + C0 + 8 * c);
+          *reinterpret_cast<uint4*>(dst + r * ST + 8 * p) = v;
+        }
       }
     }
   };
@@ -230,11 +247,7 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
       for (int bn = 0; bn < 2; ++bn) asm volatile("" : "+v"(acc[bm][bn]));
   };
 
-  for (int k = 0; k < DEPTH && k < nstages; ++k) {
-    const int64_t tk = t_begin + static_cast<int64_t>(k) * SBK;
-    load_stage(tk, I0, sA[k]);
-    if (!diag) load_stage(tk, J0, sB[k]);
-  }
+  for (int k = 0; k < DEPTH && k < nstages; ++k) load_stage(k);
   Ops P, Q;   // half-stage operand sets: P = (stage, first half), Q = (stage, second half)
   if (nstages > 0) {
     wait_copies(min(DEPTH, nstages) - 1);
@@ -263,11 +276,7 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
     mma(P);
     if (s + 1 < nstages) wait_copies(min(s + DEPTH - 1, nstages - 1) - (s + 1));
     __syncthreads();
-    if (s + DEPTH < nstages) {
-      const int64_t tn = t_begin + static_cast<int64_t>(s + DEPTH) * SBK;
-      load_stage(tn, I0, sA[(s + DEPTH) % NBUF]);
-      if (!diag) load_stage(tn, J0, sB[(s + DEPTH) % NBUF]);
-    }
+    if (s + DEPTH < nstages) load_stage(s + DEPTH);
     if (s + 1 < nstages) read_ops(s + 1, 0, P);
     mma(Q);
   }
