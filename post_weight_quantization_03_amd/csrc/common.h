@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gptq.h"
 
 #define GPTQ_HIP_TRY(expr)                         \
@@ -91,6 +93,16 @@ gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uin
 // SYRK launch timing (gptq_timing_enable / gptq_timing_read): returns the event pair to
 // record around the next SYRK launch, or nulls when timing is off.
 void timing_pair(hipEvent_t* start, hipEvent_t* stop);
+
+// A second stream per device for work that can overlap the caller's stream; two events
+// fork work onto it and join it back.  Created on first use, kept for the life of the
+// process.  Callers hold side_mutex() while they enqueue on it.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex& side_mutex();
+gptq_status side_stream(SideStream** out);   // of the current device
 
 // fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C (row-major, batched by blockIdx.z).
 struct GemmArgs {

@@ -44,6 +44,30 @@ TimingState& timing() {
 }  // namespace
 
 namespace gptq {
+namespace {
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+}  // namespace
+
+std::mutex& side_mutex() {
+  static std::mutex mu;
+  return mu;
+}
+
+gptq_status side_stream(SideStream** out) {
+  int dev = 0;
+  GPTQ_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return GPTQ_ERR_HIP;
+  SideStream& ss = g_side[dev];
+  if (ss.s == nullptr) {
+    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
+    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+  }
+  *out = &ss;
+  return GPTQ_OK;
+}
+
 void timing_pair(hipEvent_t* start, hipEvent_t* stop) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);

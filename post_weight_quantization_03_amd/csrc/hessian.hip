@@ -101,13 +101,12 @@ __device__ __forceinline__ int swz_chunk(int t, int c) { return c ^ (2 * (t & 3)
 // the matrix cores.
 //
 // partial == nullptr: H += 2 * tile (and its mirror).  Otherwise the raw tile goes to
-// partial[e][slice][tile][256][256] for syrk_reduce_kernel.  Diagonal tiles also add the
-// fp64 channel energies sum_t x^2 of their 256 channels to epart[e][slice][c].
+// partial[e][slice][tile][256][256] for syrk_reduce_kernel.
 template <bool kF16>
 __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, int d_in,
     int64_t tokens_per_split, int ksplit, float* __restrict__ H, int64_t bsh, float* __restrict__ partial,
-    double* __restrict__ epart, int ntiles) {
+    int ntiles) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][SBK * ST];
   __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][SBK * ST];
 
@@ -194,7 +193,6 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
   const int op_ch = 16 * (g16 & 1) + 4 * ra;         // + 32*block
   const int op_tok = 8 * (g16 >> 1) + rq;            // + 16*ks + 4*half
   const int nstages = static_cast<int>((t_end - t_begin + SBK - 1) / SBK);
-  double energy = 0.0;                               // diagonal tiles: channel I0 + tid
 
   auto operand = [&](const uint16_t* stage, int ch0, int tok0) -> s16x4 {
     const int ch = ch0 + op_ch;
@@ -262,17 +260,6 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
   //   phase 2: read (s+1, first half) | MFMAs (s, second half)
   for (int s = 0; s < nstages; ++s) {
     read_ops(s, 1, Q);
-    if (diag && epart != nullptr && tid < ST) {
-      // fp64 energy of channel I0 + tid over this stage's tokens (products exact in fp64)
-      const uint16_t* as = sA[s % NBUF];
-      const int ch = tid;
-#pragma unroll 8
-      for (int t = 0; t < SBK; ++t) {
-        const uint16_t v = as[t * ST + 8 * swz_chunk(t, ch >> 3) + (ch & 7)];
-        const double x = static_cast<double>(kF16 ? f16_to_f32(v) : bf16_to_f32(v));
-        energy = fma(x, x, energy);
-      }
-    }
     mma(P);
     if (s + 1 < nstages) wait_copies(min(s + DEPTH - 1, nstages - 1) - (s + 1));
     __syncthreads();
@@ -280,9 +267,6 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
     if (s + 1 < nstages) read_ops(s + 1, 0, P);
     mma(Q);
   }
-  if (diag && epart != nullptr && tid < ST && I0 + tid < d_in)
-    epart[(static_cast<int64_t>(e) * ksplit + split) * d_in + I0 + tid] = energy;
-
   // Accumulator layout of a 32x32 MFMA block: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (partial != nullptr) {
@@ -430,31 +414,37 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
     }
 }
 
-// fp64 channel energy of one token slice: part[e][split][c] = sum_t x[t][c]^2.
+// fp64 channel energies sum_t x_tc^2 of one token slice: part[e][slice][c].  A thread
+// owns V = 16 / sizeof(T) consecutive channels and reads them 16 bytes at a time (the
+// squares are exact in fp64).
 template <typename T>
 __global__ __launch_bounds__(256) void channel_energy_kernel(const T* __restrict__ X, int64_t ldx,
                                                              int64_t bsx, int64_t n_tokens, int d_in,
                                                              int64_t tokens_per_split,
                                                              double* __restrict__ part) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  constexpr int V = 16 / sizeof(T);
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * V;
   const int split = blockIdx.y, e = blockIdx.z;
-  if (c >= d_in) return;
+  if (c0 >= d_in) return;
   const int64_t t0 = static_cast<int64_t>(split) * tokens_per_split;
   const int64_t t1 = min(n_tokens, t0 + tokens_per_split);
-  const T* Xe = X + static_cast<int64_t>(e) * bsx + c;
-  double acc0 = 0.0, acc1 = 0.0;
-  int64_t t = t0;
-  for (; t + 1 < t1; t += 2) {
-    const double a = static_cast<double>(load_as_f32(Xe + t * ldx));
-    const double b = static_cast<double>(load_as_f32(Xe + (t + 1) * ldx));
-    acc0 = fma(a, a, acc0);
-    acc1 = fma(b, b, acc1);
+  const T* Xe = X + static_cast<int64_t>(e) * bsx + c0;
+  double acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.0;
+#pragma unroll 4
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(Xe + t * ldx);
+    const T* x = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const double xv = static_cast<double>(load_as_f32(x + v));
+      acc[v] = fma(xv, xv, acc[v]);
+    }
   }
-  if (t < t1) {
-    const double a = static_cast<double>(load_as_f32(Xe + t * ldx));
-    acc0 = fma(a, a, acc0);
-  }
-  part[(static_cast<int64_t>(e) * gridDim.y + split) * d_in + c] = acc0 + acc1;
+  double* dst = part + (static_cast<int64_t>(e) * gridDim.y + split) * d_in + c0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) dst[v] = acc[v];
 }
 
 __global__ __launch_bounds__(256) void channel_energy_reduce_kernel(const double* __restrict__ part,
@@ -466,6 +456,7 @@ __global__ __launch_bounds__(256) void channel_energy_reduce_kernel(const double
   const int e = blockIdx.y;
   if (c < d_in) {
     double s = 0.0;
+#pragma unroll 8
     for (int k = 0; k < nsplit; ++k) s += part[(static_cast<int64_t>(e) * nsplit + k) * d_in + c];
     diag_key[static_cast<int64_t>(e) * d_in + c] += 2.0 * s;
   }
@@ -502,16 +493,14 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
     pl.ksplit = static_cast<int>((n_tokens + pl.kchunk - 1) / pl.kchunk);
     if (pl.ksplit < 1) pl.ksplit = 1;
   }
-  if (mfma) {
-    pl.esplit = pl.ksplit;
-    pl.echunk = pl.kchunk;
-    return pl;
-  }
-  const int cblocks = (d_in + 255) / 256;
-  const int64_t ewant = (2048 + static_cast<int64_t>(cblocks) * batch - 1) /
+  // energy kernel: 16-byte loads of 16 / elem_bytes channels per thread, ~1024 workgroups,
+  // at least 256 tokens per slice, at most 256 slices (their sum is one thread per channel)
+  const int vec = mfma ? 8 : 4;
+  const int cblocks = (d_in + 256 * vec - 1) / (256 * vec);
+  const int64_t ewant = (1024 + static_cast<int64_t>(cblocks) * batch - 1) /
                         (static_cast<int64_t>(cblocks) * batch);
   const int64_t ecap = std::max<int64_t>(1, n_tokens / 256);
-  pl.esplit = static_cast<int>(std::min<int64_t>(std::min(ewant, ecap), 1024));
+  pl.esplit = static_cast<int>(std::min<int64_t>(std::min(ewant, ecap), 256));
   pl.echunk = (n_tokens + pl.esplit - 1) / pl.esplit;
   if (pl.echunk == 0) pl.echunk = 1;
   pl.esplit = static_cast<int>(std::max<int64_t>(1, (n_tokens + pl.echunk - 1) / pl.echunk));
@@ -554,7 +543,24 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
   plan_bytes(pl, batch, d_in, &partial, &epart, ws);
 
   const dim3 blk(256);
+  const dim3 egrid((d_in + 256 * (mfma ? 8 : 4) - 1) / (256 * (mfma ? 8 : 4)), pl.esplit, batch);
   if (mfma) {
+    // The fp64 channel energies (memory-bound) run on the side stream next to the SYRK
+    // (matrix-core bound); the main stream joins them before the energy reduction.
+    std::lock_guard<std::mutex> lk(side_mutex());
+    SideStream* ss = nullptr;
+    if (const gptq_status st = side_stream(&ss); st != GPTQ_OK) return st;
+    GPTQ_HIP_TRY(hipEventRecord(ss->fork, stream));
+    GPTQ_HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
+    if (x_dtype == GPTQ_F16) {
+      GPTQ_LAUNCH(channel_energy_kernel<F16>, egrid, blk, 0, ss->s, static_cast<const F16*>(X), ldx, bsx, n_tokens,
+                  d_in, pl.echunk, epart);
+    } else {
+      GPTQ_LAUNCH(channel_energy_kernel<BF16>, egrid, blk, 0, ss->s, static_cast<const BF16*>(X), ldx, bsx,
+                  n_tokens, d_in, pl.echunk, epart);
+    }
+    GPTQ_HIP_TRY(hipEventRecord(ss->join, ss->s));
+
     const dim3 sblk(SYRK_THREADS);
     const dim3 grid(pl.ntiles * pl.ksplit, batch);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
@@ -564,21 +570,22 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
       GPTQ_LAUNCH(syrk_mfma_kernel<true>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit, H,
-                  bsh, part, epart, pl.ntiles);
+                  bsh, part, pl.ntiles);
     } else {
       GPTQ_LAUNCH(syrk_mfma_kernel<false>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
-                  H, bsh, part, epart, pl.ntiles);
+                  H, bsh, part, pl.ntiles);
     }
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
     if (pl.ksplit > 1) {
       GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
                   H, bsh);
     }
+    GPTQ_HIP_TRY(hipStreamWaitEvent(stream, ss->join, 0));
   } else {
     GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream, static_cast<const float*>(X), ldx, bsx,
                 n_tokens, d_in, H, bsh);
-    GPTQ_LAUNCH(channel_energy_kernel<float>, dim3((d_in + 255) / 256, pl.esplit, batch), blk, 0, stream,
-                static_cast<const float*>(X), ldx, bsx, n_tokens, d_in, pl.echunk, epart);
+    GPTQ_LAUNCH(channel_energy_kernel<float>, egrid, blk, 0, stream, static_cast<const float*>(X), ldx, bsx, n_tokens,
+                d_in, pl.echunk, epart);
   }
   GPTQ_LAUNCH(channel_energy_reduce_kernel, dim3((d_in + 255) / 256, batch), blk, 0, stream, epart,
               pl.esplit, d_in, diag_key, n_seen, n_tokens);

@@ -17,7 +17,6 @@
 // kernel); everything else is fp32 matrix-core products.  A non-positive or non-finite pivot sets a device flag that
 // the host reads back (GPTQ_ERR_NOT_SPD).
 #include <algorithm>
-#include <mutex>
 
 #include "common.h"
 
@@ -409,31 +408,6 @@ PrepWs carve(void* ws, int batch, int d_in) {
   return w;
 }
 
-// A second stream per device takes the products that are off the critical path of the
-// recursion; two events fork work onto it and join it back.  Created on first use, kept
-// for the life of the process.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-gptq_status side_stream(SideStream** out) {
-  int dev = 0;
-  GPTQ_HIP_TRY(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDevices) return GPTQ_ERR_HIP;
-  SideStream& ss = g_side[dev];
-  if (ss.s == nullptr) {
-    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
-    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
-    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
-  }
-  *out = &ss;
-  return GPTQ_OK;
-}
-
 // Recursive Cholesky with the inverse, over the block range [b0, b1) of A (in place):
 //   [A11  .  ]   [L11  0 ]            L11, L11^-1 = recurse(A11)
 //   [A21 A22 ] = [L21 L22] [..]^T     L21 = A21 L11^-T           (product with L11^-1)
@@ -531,7 +505,7 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
               w.lambda, d_in, w.A);
   // L is built in the U buffer (same shape), then replaced by U at the end.
   {
-    std::lock_guard<std::mutex> lk(g_side_mu);
+    std::lock_guard<std::mutex> lk(side_mutex());
     Sched sc{stream, nullptr, d_in / NB, batch};
     gptq_status st = side_stream(&sc.side);
     if (st != GPTQ_OK) return st;
