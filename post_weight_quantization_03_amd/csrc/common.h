@@ -114,6 +114,9 @@ struct GemmArgs {
   int transB;
   int flags;                         // GemmFlags
   int batch;
+  // optional inner batch: product z = zo * batch2 + zi sits at zo * s + zi * s2
+  int batch2 = 1;
+  int64_t sA2 = 0, sB2 = 0, sC2 = 0;
 };
 enum GemmFlags {
   kLowerOut = 1,   // C square: only tiles on or below the diagonal are computed

@@ -1,5 +1,6 @@
 // fp32 GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32):
-//   C = alpha * op(A) * op(B) + beta * C,   A [M, K], op(B) = B [K, N] or B^T (B [N, K]).
+//   C = alpha * op(A) * op(B) + beta * C,   A [M, K], op(B) = B [K, N] or B^T (B [N, K]),
+// batched over blockIdx.z (two nested batch strides).
 //
 // Used for the blocked Cholesky (panel solve as a product with the inverted diagonal
 // block, trailing symmetric update), the triangular inverse, and GPTQ's lazy batch update
@@ -29,10 +30,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int RQ = GT / 32;  // row-vector loads per thread (rows of 32 k)
   const int n0 = blockIdx.x * GT, m0 = blockIdx.y * GT;
   if ((g.flags & kLowerOut) && n0 > m0) return;
-  const int z = blockIdx.z;
-  const float* A = g.A + static_cast<int64_t>(z) * g.sA;
-  const float* B = g.B + static_cast<int64_t>(z) * g.sB;
-  float* C = g.C + static_cast<int64_t>(z) * g.sC;
+  const int zo = blockIdx.z / g.batch2, zi = blockIdx.z % g.batch2;
+  const float* A = g.A + static_cast<int64_t>(zo) * g.sA + static_cast<int64_t>(zi) * g.sA2;
+  const float* B = g.B + static_cast<int64_t>(zo) * g.sB + static_cast<int64_t>(zi) * g.sB2;
+  float* C = g.C + static_cast<int64_t>(zo) * g.sC + static_cast<int64_t>(zi) * g.sC2;
 
   int kb = 0, ke = g.K;
   if (g.flags & kALower) ke = min(ke, m0 + GT);
@@ -181,14 +182,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }  // namespace
 
 gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
-  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return GPTQ_OK;
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0 || g.batch2 <= 0) return GPTQ_OK;
+  const int nz = g.batch * g.batch2;
   // 128-wide tiles when they give every CU two workgroups, or one for a plain product
   // (triangular operands leave some tiles with far less work, a lower-only output skips
   // half of them); else 64-wide
-  const int64_t tiles128 = static_cast<int64_t>((g.N + 127) / 128) * ((g.M + 127) / 128) * g.batch;
+  const int64_t tiles128 = static_cast<int64_t>((g.N + 127) / 128) * ((g.M + 127) / 128) * nz;
   const bool big = tiles128 >= 512 || (g.flags == 0 && tiles128 >= 256);
   const int T = big ? 128 : 64;
-  const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, g.batch);
+  const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, nz);
   if (big) {
     if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_f32_kernel<false, 128>), grid, dim3(256), 0, stream, g);

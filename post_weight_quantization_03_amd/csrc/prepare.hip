@@ -12,9 +12,10 @@
 //      positive-diagonal upper factor the pages obtain with chol / cholesky_inverse / chol,
 //      at 2/3 d^3 instead of 4/3 d^3 flops.
 //
-// Cholesky and inverse together by recursive halving (chol_inv below): one workgroup
-// factors and inverts each 128-column diagonal block in LDS (the same halving, inside the
-// kernel); everything else is fp32 matrix-core products.  A non-positive or non-finite pivot sets a device flag that
+// Cholesky blocked by 128 columns (chol_blocked below), then the triangular inverse by
+// doubling (trtri_doubling): one workgroup factors and inverts each 128-column diagonal
+// block in LDS (by recursive halving inside the kernel); everything else is fp32
+// matrix-core products.  A non-positive or non-finite pivot sets a device flag that
 // the host reads back (GPTQ_ERR_NOT_SPD).
 #include <algorithm>
 
@@ -126,8 +127,8 @@ __global__ __launch_bounds__(256) void gather_reversed_kernel(const float* __res
 // Factor the diagonal block at (k0, k0) of A: writes L_kk into Lbuf and L_kk^-1 into Linv
 // (full 128x128 blocks, zeros above the diagonal).  Only the lower triangle of A is read.
 //
-// The block and its inverse stay in LDS for the whole kernel, and the same halving as
-// chol_inv below runs inside it down to 16-column leaves:
+// The block and its inverse stay in LDS for the whole kernel, and a recursive halving
+// runs inside it down to 16-column leaves:
 //   node(o, S):  node(o, S/2);  L21 = A21 X11^T;  S22 = A22 - L21 L21^T and T = L21 X11;
 //                node(o + S/2, S/2);  X21 = -X22 T
 // (X = L^-1).  A 16-column leaf is factored and inverted by one wave with the 16 rows in
@@ -369,17 +370,14 @@ __global__ __launch_bounds__(256) void reverse_to_upper_kernel(const float* __re
   U[static_cast<int64_t>(e) * bsu + static_cast<int64_t>(i) * d_in + j] = v;
 }
 
-// T = L21 L11^-1 of a node at recursion depth t lives at t_offset(t) of the T workspace:
-// one buffer per depth, because the T of a node is produced on the side stream while its
-// second half (deeper nodes) runs.  A node at depth t spans at most ceil(nb / 2^t) blocks.
-size_t t_offset(int depth, int nb, int batch) {
-  size_t off = 0;
-  for (int t = 0, span = nb; t < depth && span > 1; ++t) {
-    const size_t h2 = static_cast<size_t>((span + 1) / 2) * NB;
-    off += static_cast<size_t>(batch) * h2 * h2;
-    span = (span + 1) / 2;
+// Floats of T per problem for trtri_doubling: the largest level, (full groups + 1) h^2.
+size_t trtri_t_floats(int nb) {
+  size_t m = 0;
+  for (int hb = 1; hb < nb; hb *= 2) {
+    const size_t h = static_cast<size_t>(hb) * NB;
+    m = std::max(m, static_cast<size_t>(nb / (2 * hb) + 1) * h * h);
   }
-  return off;
+  return m;
 }
 
 struct PrepWs {
@@ -403,80 +401,118 @@ PrepWs carve(void* ws, int batch, int d_in) {
   w.flag = cv.take<int>(batch);
   w.A = cv.take<float>(batch * dd);
   w.Linv = cv.take<float>(batch * dd);
-  w.T = cv.take<float>(t_offset(64, d_in / NB, batch));
+  w.T = cv.take<float>(static_cast<size_t>(batch) * trtri_t_floats(d_in / NB));
   w.bytes = cv.used;
   return w;
 }
 
-// Recursive Cholesky with the inverse, over the block range [b0, b1) of A (in place):
-//   [A11  .  ]   [L11  0 ]            L11, L11^-1 = recurse(A11)
-//   [A21 A22 ] = [L21 L22] [..]^T     L21 = A21 L11^-T           (product with L11^-1)
-//                                     S   = A22 - L21 L21^T      (lower tiles, in place)
-//                                     L22, L22^-1 = recurse(S)
-//   L^-1 = [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]].
-// Leaves are single 128-column blocks (potrf_block_kernel).  Every product runs on the
-// fp32 matrix cores with triangular operands trimming the K range; most of the flops land
-// in the large products near the top of the recursion.
-//
-// The chain leaf -> L21 -> S -> leaf ... is serial and mostly leaves the GPU idle, so
-// T = L21 L11^-1, needed only by the node's last product, runs on the side stream while
-// the second half recurses; the main stream waits for it just before that product.
+// Cholesky of A (lower, in place) into L, blocked by 128 columns, right-looking with a
+// one-block lookahead.  For each block column k, on the main stream:
+//   leaf(k):  L_kk and X_kk = L_kk^-1 from the updated diagonal block (potrf_block_kernel);
+//   panel(k): L[k+1:, k] = A[k+1:, k] X_kk^T;
+//   near(k):  A[k+1:, k+1] -= L[k+1:, k] L[k+1, k]^T  (the next block column, so that
+//             leaf(k+1) and panel(k+1) can start);
+// and on the side stream, overlapping leaf(k+1) and panel(k+1):
+//   far(k):   A[k+2:, k+2:] -= L[k+2:, k] L[k+2:, k]^T  (lower tiles).
+// far(k) starts once panel(k) is done; near(k+1) writes block column k+2, which far(k)
+// also writes, so it waits for far(k).  Every block receives the updates of all earlier
+// panels before it is factored: the last one from near, the others from far.
 struct Sched {
   hipStream_t main;
   SideStream* side;
   int nb, batch;
 };
 
-gptq_status chol_inv(int b0, int b1, int depth, int d_in, float* A, float* L, int64_t bsl, float* Linv,
-                     float* Tbase, int* flag, const Sched& sc) {
-  const int batch = sc.batch;
+float* block_at(float* base, int d_in, int bi, int bj) {
+  return base + static_cast<int64_t>(bi) * NB * d_in + static_cast<int64_t>(bj) * NB;
+}
+
+gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc) {
+  const int nb = sc.nb, batch = sc.batch;
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
-  hipStream_t stream = sc.main;
-  if (b1 - b0 == 1) {
-    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, stream, A, L, bsl, Linv, d_in, b0 * NB, flag);
-    return GPTQ_OK;
+  hipStream_t s0 = sc.main, s1 = sc.side->s;
+  for (int k = 0; k < nb; ++k) {
+    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
+    const int rest = nb - k - 1;   // block rows below the diagonal block k
+    if (rest == 0) break;
+    gptq_status st;
+    GemmArgs g{};
+    g.batch = batch;
+    g.M = rest * NB; g.N = NB; g.K = NB;
+    g.A = block_at(A, d_in, k + 1, k); g.lda = d_in; g.sA = dd;
+    g.B = block_at(Linv, d_in, k, k); g.ldb = d_in; g.sB = dd;
+    g.C = block_at(L, d_in, k + 1, k); g.ldc = d_in; g.sC = bsl;
+    g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower;
+    if ((st = gemm_f32(g, s0)) != GPTQ_OK) return st;
+    GPTQ_HIP_TRY(hipEventRecord(sc.side->fork, s0));           // panel(k) done
+    if (k > 0) GPTQ_HIP_TRY(hipStreamWaitEvent(s0, sc.side->join, 0));   // far(k-1) done
+    GemmArgs n{};
+    n.batch = batch;
+    n.M = rest * NB; n.N = NB; n.K = NB;
+    n.A = block_at(L, d_in, k + 1, k); n.lda = d_in; n.sA = bsl;
+    n.B = n.A; n.ldb = d_in; n.sB = bsl;                         // rows of L[k+1, k]
+    n.C = block_at(A, d_in, k + 1, k + 1); n.ldc = d_in; n.sC = dd;
+    n.alpha = -1.0f; n.beta = 1.0f; n.transB = 1; n.flags = 0;
+    if ((st = gemm_f32(n, s0)) != GPTQ_OK) return st;
+    if (rest >= 2) {
+      GPTQ_HIP_TRY(hipStreamWaitEvent(s1, sc.side->fork, 0));
+      GemmArgs f{};
+      f.batch = batch;
+      f.M = (rest - 1) * NB; f.N = (rest - 1) * NB; f.K = NB;
+      f.A = block_at(L, d_in, k + 2, k); f.lda = d_in; f.sA = bsl;
+      f.B = f.A; f.ldb = d_in; f.sB = bsl;
+      f.C = block_at(A, d_in, k + 2, k + 2); f.ldc = d_in; f.sC = dd;
+      f.alpha = -1.0f; f.beta = 1.0f; f.transB = 1; f.flags = kLowerOut;
+      if ((st = gemm_f32(f, s1)) != GPTQ_OK) return st;
+      GPTQ_HIP_TRY(hipEventRecord(sc.side->join, s1));
+    }
   }
-  const int bm = b0 + (b1 - b0) / 2;
-  const int o1 = b0 * NB, o2 = bm * NB, h1 = (bm - b0) * NB, h2 = (b1 - bm) * NB;
-  float* T = Tbase + t_offset(depth, sc.nb, batch);
-  gptq_status st = chol_inv(b0, bm, depth + 1, d_in, A, L, bsl, Linv, Tbase, flag, sc);
-  if (st != GPTQ_OK) return st;
-  GemmArgs g{};
-  // L21 = A21 * (L11^-1)^T
-  g.M = h2; g.N = h1; g.K = h1;
-  g.A = A + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = dd;
-  g.B = Linv + static_cast<int64_t>(o1) * d_in + o1; g.ldb = d_in; g.sB = dd;
-  g.C = L + static_cast<int64_t>(o2) * d_in + o1; g.ldc = d_in; g.sC = bsl;
-  g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower; g.batch = batch;
-  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
-  // T = L21 * L11^-1 on the side stream (L11^-1 lower: the K range of an output column starts at it)
-  GPTQ_HIP_TRY(hipEventRecord(sc.side->fork, stream));
-  GPTQ_HIP_TRY(hipStreamWaitEvent(sc.side->s, sc.side->fork, 0));
-  GemmArgs t = g;
-  t.M = h2; t.N = h1; t.K = h1;
-  t.A = L + static_cast<int64_t>(o2) * d_in + o1; t.lda = d_in; t.sA = bsl;
-  t.B = Linv + static_cast<int64_t>(o1) * d_in + o1; t.ldb = d_in; t.sB = dd;
-  t.C = T; t.ldc = h1; t.sC = static_cast<int64_t>(h2) * h1;
-  t.alpha = 1.0f; t.beta = 0.0f; t.transB = 0; t.flags = kBLower;
-  if ((st = gemm_f32(t, sc.side->s)) != GPTQ_OK) return st;
-  // S = A22 - L21 L21^T (lower tiles)
-  g.M = h2; g.N = h2; g.K = h1;
-  g.A = L + static_cast<int64_t>(o2) * d_in + o1; g.lda = d_in; g.sA = bsl;
-  g.B = g.A; g.ldb = d_in; g.sB = bsl;
-  g.C = A + static_cast<int64_t>(o2) * d_in + o2; g.ldc = d_in; g.sC = dd;
-  g.alpha = -1.0f; g.beta = 1.0f; g.transB = 1; g.flags = kLowerOut;
-  if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
-  if ((st = chol_inv(bm, b1, depth + 1, d_in, A, L, bsl, Linv, Tbase, flag, sc)) != GPTQ_OK) return st;
-  // join: the side stream is in order, so its latest point covers this node's T
-  GPTQ_HIP_TRY(hipEventRecord(sc.side->join, sc.side->s));
-  GPTQ_HIP_TRY(hipStreamWaitEvent(stream, sc.side->join, 0));
-  // Linv21 = -L22^-1 * T   (L22^-1 lower: the K range of an output row ends at it)
-  g.M = h2; g.N = h1; g.K = h2;
-  g.A = Linv + static_cast<int64_t>(o2) * d_in + o2; g.lda = d_in; g.sA = dd;
-  g.B = T; g.ldb = h1; g.sB = static_cast<int64_t>(h2) * h1;
-  g.C = Linv + static_cast<int64_t>(o2) * d_in + o1; g.ldc = d_in; g.sC = dd;
-  g.alpha = -1.0f; g.beta = 0.0f; g.transB = 0; g.flags = kALower;
-  return gemm_f32(g, stream);
+  return GPTQ_OK;
+}
+
+// X = L^-1 from L and its inverted diagonal blocks, by doubling: at the level of groups of
+// 2 hb blocks (hb = 1, 2, 4, ...), every group [o, o + 2h) whose halves are inverted gets
+//   T = L21 X11,   X21 = -X22 T
+// (X11 = L11^-1 lower: the K range of an output column of T starts at it; X22 lower: the
+// K range of an output row of X21 ends at it).  All full groups of a level go in one
+// batched product each; a ragged last group (a full first half and a shorter second half,
+// itself inverted at the level below) gets its own pair.
+gptq_status trtri_doubling(int d_in, const float* L, int64_t bsl, float* Linv, float* T, int nb, int batch,
+                           hipStream_t stream) {
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  for (int hb = 1; hb < nb; hb *= 2) {
+    const int h = hb * NB;
+    const int full = nb / (2 * hb);
+    const int tail = nb - full * 2 * hb;                       // blocks of the last group
+    const int64_t tstride = static_cast<int64_t>(full + 1) * h * h;   // T floats per problem
+    auto pair = [&](int o_blk, int h2, int groups, float* Tg) -> gptq_status {
+      const int64_t gs = static_cast<int64_t>(2 * h) * (d_in + 1);   // next group, same level
+      const int o = o_blk * NB;
+      gptq_status st;
+      GemmArgs t{};
+      t.batch = batch; t.batch2 = groups;
+      t.M = h2; t.N = h; t.K = h;
+      t.A = L + static_cast<int64_t>(o + h) * d_in + o; t.lda = d_in; t.sA = bsl; t.sA2 = gs;
+      t.B = Linv + static_cast<int64_t>(o) * d_in + o; t.ldb = d_in; t.sB = dd; t.sB2 = gs;
+      t.C = Tg; t.ldc = h; t.sC = tstride; t.sC2 = static_cast<int64_t>(h) * h;
+      t.alpha = 1.0f; t.beta = 0.0f; t.transB = 0; t.flags = kBLower;
+      if ((st = gemm_f32(t, stream)) != GPTQ_OK) return st;
+      GemmArgs x{};
+      x.batch = batch; x.batch2 = groups;
+      x.M = h2; x.N = h; x.K = h2;
+      x.A = Linv + static_cast<int64_t>(o + h) * d_in + o + h; x.lda = d_in; x.sA = dd; x.sA2 = gs;
+      x.B = Tg; x.ldb = h; x.sB = tstride; x.sB2 = static_cast<int64_t>(h) * h;
+      x.C = Linv + static_cast<int64_t>(o + h) * d_in + o; x.ldc = d_in; x.sC = dd; x.sC2 = gs;
+      x.alpha = -1.0f; x.beta = 0.0f; x.transB = 0; x.flags = kALower;
+      return gemm_f32(x, stream);
+    };
+    gptq_status st;
+    if (full > 0 && (st = pair(0, h, full, T)) != GPTQ_OK) return st;
+    // the T of the ragged group sits after those of the full groups
+    if (tail > hb && (st = pair(full * 2 * hb, (tail - hb) * NB, 1, T + static_cast<int64_t>(full) * h * h)) != GPTQ_OK)
+      return st;
+  }
+  return GPTQ_OK;
 }
 
 }  // namespace
@@ -509,8 +545,8 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
     Sched sc{stream, nullptr, d_in / NB, batch};
     gptq_status st = side_stream(&sc.side);
     if (st != GPTQ_OK) return st;
-    st = chol_inv(0, d_in / NB, 0, d_in, w.A, U, bsu, w.Linv, w.T, w.flag, sc);
-    if (st != GPTQ_OK) return st;
+    if ((st = chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc)) != GPTQ_OK) return st;
+    if ((st = trtri_doubling(d_in, U, bsu, w.Linv, w.T, d_in / NB, batch, stream)) != GPTQ_OK) return st;
   }
   GPTQ_LAUNCH(reverse_to_upper_kernel, dim3(cb, d_in, batch), blk, 0, stream, w.Linv, d_in, U, bsu);
 
