@@ -163,20 +163,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 
   // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // With beta != 0 the 16 old values of a block are all loaded before any of its stores:
+  // element by element, every load would have to wait for the previous store (the
+  // compiler cannot tell that they never overlap).
+  const bool has_beta = g.beta != 0.0f;
 #pragma unroll
   for (int bm = 0; bm < MB; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < MB; ++bn)
+    for (int bn = 0; bn < MB; ++bn) {
+      const int n = n0 + (GT / 2) * wn + 32 * bn + l32;
+      float old[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + (GT / 2) * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const int n = n0 + (GT / 2) * wn + 32 * bn + l32;
+        old[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + (GT / 2) * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
         if (m < g.M && n < g.N) {
-          float* c = C + static_cast<int64_t>(m) * g.ldc + n;
           const float v = g.alpha * acc[bm][bn][r];
-          *c = (g.beta != 0.0f) ? fmaf(g.beta, *c, v) : v;
+          C[static_cast<int64_t>(m) * g.ldc + n] = has_beta ? fmaf(g.beta, old[r], v) : v;
         }
       }
+    }
 }
 
 }  // namespace
