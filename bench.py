@@ -26,7 +26,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "GPTQ layer quantize ms & Gweights/s; SYRK+trailing GEMM % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3      # MI355X fp32 matrix
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 (vector with packed math, and matrix)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -193,9 +193,12 @@ def main():
     launches_per_step = (spec.n_tokens + chunk - 1) // chunk
     syrk_flops = E * spec.d_in * (spec.d_in + 1) * min(chunk, spec.n_tokens)
     syrk_ms = syrk_total_ms / max(syrk_launches, 1)
-    achieved = syrk_flops / (syrk_ms / 1e3) / 1e12
-    peak = PEAK_BF16_TFLOPS if spec.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
-    roof = dict(bound="mfma", kernel="syrk_mfma_kernel", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+    achieved = syrk_flops / (syrk_ms / 1e3) / 1e12 if syrk_ms > 0 else 0.0
+    mfma = spec.dtype in ("bf16", "f16")
+    # fp32 inputs run the vector-ALU SYRK: its peak is the chip's fp32 vector rate
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_TFLOPS
+    roof = dict(bound="mfma" if mfma else "alu", kernel="syrk_mfma_kernel" if mfma else "syrk_f32_kernel",
+                achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                 frac=round(achieved / peak, 4), traffic=syrk_traffic(spec.name) if chunk >= spec.n_tokens else None,
                 launch_ms=round(syrk_ms, 4), launches=syrk_launches, launches_per_step=launches_per_step,
                 flops_per_launch=syrk_flops)

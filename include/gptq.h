@@ -178,7 +178,8 @@ size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
 
 /* Measurement hook for the Hessian SYRK kernel (the dominant kernel of the path).
  * While enabled (on != 0), every gptq_accumulate_hessian call records a pair of HIP events
- * on its stream immediately around its SYRK kernel launch.  gptq_timing_read waits for the
+ * on its stream immediately around its SYRK kernel launch (the matrix-core kernel for
+ * bf16/fp16 inputs, the vector-ALU kernel for fp32 inputs).  gptq_timing_read waits for the
  * recorded events, returns the summed elapsed milliseconds and the number of launches since
  * the previous read, and forgets them.  Events are created by the library on first use and
  * reused; the hook is process-wide and not meant for concurrent callers. */

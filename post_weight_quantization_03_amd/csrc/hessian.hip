@@ -582,8 +582,12 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     }
     GPTQ_HIP_TRY(hipStreamWaitEvent(stream, ss->join, 0));
   } else {
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    timing_pair(&ev0, &ev1);
+    if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream, static_cast<const float*>(X), ldx, bsx,
                 n_tokens, d_in, H, bsh);
+    if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
     GPTQ_LAUNCH(channel_energy_kernel<float>, egrid, blk, 0, stream, static_cast<const float*>(X), ldx, bsx, n_tokens,
                 d_in, pl.echunk, epart);
   }
