@@ -18,16 +18,20 @@
 namespace gptq {
 namespace {
 
-constexpr int GK = 32;
-
 // TT = output tile edge (128 or 64); each of the 4 waves owns a (TT/2) x (TT/2) quarter as
-// MB x MB blocks of 32 x 32.
+// MB x MB blocks of 32 x 32.  The 64-wide tile takes 64 k per stage: with one workgroup per
+// CU its stage is otherwise too short to cover the latency of the next stage's loads.
 template <bool kTransB, int TT>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int GT = TT;
-  constexpr int GP = GT + 4;  // LDS row length
+  constexpr int GK = TT == 64 ? 64 : 32;
+  // LDS row lengths.  Rows written by the transposing scalar stores get an odd length, so
+  // the 8 k rows x 4 tile rows that half a wave writes fall on 32 different banks; rows
+  // written as float4 (B already k-major) keep 16-byte alignment.
+  constexpr int GPA = GT + 1;
+  constexpr int GPB = kTransB ? GT + 1 : GT + 4;
   constexpr int MB = TT / 64;
-  constexpr int RQ = GT / 32;  // row-vector loads per thread (rows of 32 k)
+  constexpr int RQ = GT * GK / 1024;  // float4 loads per thread per operand and stage
   const int n0 = blockIdx.x * GT, m0 = blockIdx.y * GT;
   if ((g.flags & kLowerOut) && n0 > m0) return;
   const int zo = blockIdx.z / g.batch2, zi = blockIdx.z % g.batch2;
@@ -41,19 +45,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if (g.flags & kBLower) kb = max(kb, n0);
   kb = kb / GK * GK;
 
-  __shared__ __attribute__((aligned(16))) float sA[2][GK][GP];
-  __shared__ __attribute__((aligned(16))) float sB[2][GK][GP];
+  __shared__ __attribute__((aligned(16))) float sA[2][GK][GPA];
+  __shared__ __attribute__((aligned(16))) float sB[2][GK][GPB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
   float4 ra[RQ], rb[RQ];
-  // A tile [GT rows][32 k]: thread loads rows (tid>>3) + 32q, k = 4*(tid&7)..+3
+  // Row-major tile [GT rows][GK k] read as float4: half a wave covers 4 rows x 8 k-vectors
+  // (row lr + RS q, k 4 lc .. 4 lc + 3), which makes its transposing LDS stores conflict-free.
+  constexpr int RS = 1024 / GK;  // rows per pass of the workgroup
+  const int lc = GK == 32 ? (lane & 7) : (lane & 7) + 8 * (lane >> 5);
+  const int lr = GK == 32 ? (lane >> 3) + 8 * wave : ((lane >> 3) & 3) + 4 * wave;
   auto load_rows = [&](const float* P, int64_t ld, int r0, int rlim, int k0, float4* r) {
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
-      const int row = r0 + (tid >> 3) + 32 * q;
-      const int k = k0 + 4 * (tid & 7);
+      const int row = r0 + lr + RS * q;
+      const int k = k0 + 4 * lc;
       if (row < rlim && k < ke) {
         r[q] = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(row) * ld + k);
         if (k + 4 > ke) {  // partial K vector: zero the tail
@@ -66,18 +74,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
     }
   };
-  auto store_rows = [&](float (*s)[GP], const float4* r) {
+  auto store_rows = [&](auto s, const float4* r) {
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
-      const int row = (tid >> 3) + 32 * q;
-      const int k = 4 * (tid & 7);
+      const int row = lr + RS * q;
+      const int k = 4 * lc;
       s[k + 0][row] = r[q].x;
       s[k + 1][row] = r[q].y;
       s[k + 2][row] = r[q].z;
       s[k + 3][row] = r[q].w;
     }
   };
-  // B tile [32 k][GT n] (no transpose): thread loads k = tid / (GT/4) + (256*4/GT) q,
+  // B tile [GK k][GT n] (no transpose): thread loads k = tid / (GT/4) + (256*4/GT) q,
   // n = 4 * (tid % (GT/4))
   constexpr int NV = GT / 4;        // float4 per k row
   constexpr int KS = 256 / NV;      // k rows covered by one pass of the block
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
     }
   };
-  auto store_kmajor = [&](float (*s)[GP], const float4* r) {
+  auto store_kmajor = [&](float (*s)[GPB], const float4* r) {
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
       const int k = tid / NV + KS * q;
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     if constexpr (kTransB) load_rows(B, g.ldb, n0, g.N, k0, rb);
     else load_kmajor(k0, rb);
   };
-  auto store_b = [&](float (*s)[GP]) {
+  auto store_b = [&](float (*s)[GPB]) {
     if constexpr (kTransB) store_rows(s, rb);
     else store_kmajor(s, rb);
   };

@@ -102,25 +102,68 @@ __global__ __launch_bounds__(256) void damping_kernel(const double* __restrict__
 }
 
 // A[r][c] = H[p(r)][p(c)] with p(r) = perm[d-1-r]; diagonal key[p(r)] + lambda.
+// Only the blocks on and below the 128-block diagonal are written: nothing reads the others.
+// The reversed permutation of the problem and one source row of H are staged in LDS, so H is
+// read row by row in 16-byte vectors and the scatter happens in LDS.  kVec: H rows are
+// 16-byte aligned.  DMAX bounds d_in.
+constexpr int GATHER_ROWS = 4;  // output rows per workgroup
+template <int DMAX, bool kVec>
 __global__ __launch_bounds__(256) void gather_reversed_kernel(const float* __restrict__ H, int64_t bsh,
                                                               const int32_t* __restrict__ perm,
                                                               const double* __restrict__ key,
                                                               const double* __restrict__ lambda, int d_in,
                                                               float* __restrict__ A) {
+  __shared__ __attribute__((aligned(16))) float srow[DMAX];
+  __shared__ uint16_t sidx[DMAX];
+  const int e = blockIdx.y, t = threadIdx.x;
+  const int32_t* pe = perm + static_cast<int64_t>(e) * d_in;
+  // indices are clamped so that a malformed permutation can never address outside H
+  for (int c = t; c < d_in; c += 256) sidx[c] = static_cast<uint16_t>(min(max(pe[d_in - 1 - c], 0), d_in - 1));
+  const float* He = H + static_cast<int64_t>(e) * bsh;
+  for (int i = 0; i < GATHER_ROWS; ++i) {
+    const int r = blockIdx.x * GATHER_ROWS + i;
+    if (r >= d_in) break;
+    __syncthreads();  // sidx written / the previous row fully consumed
+    const int pr = sidx[r];
+    const float* src = He + static_cast<int64_t>(pr) * d_in;
+    if constexpr (kVec) {
+      for (int c4 = t; c4 < d_in / 4; c4 += 256)
+        reinterpret_cast<float4*>(srow)[c4] = reinterpret_cast<const float4*>(src)[c4];
+    } else {
+      for (int c = t; c < d_in; c += 256) srow[c] = src[c];
+    }
+    __syncthreads();
+    const int cend = min(d_in, (r / NB + 1) * NB);
+    const float dg = static_cast<float>(key[static_cast<int64_t>(e) * d_in + pr] + lambda[e]);
+    float* dst = A + (static_cast<int64_t>(e) * d_in + r) * d_in;
+    for (int c = 4 * t; c < cend; c += 1024) {
+      float4 v = make_float4(srow[sidx[c]], srow[sidx[c + 1]], srow[sidx[c + 2]], srow[sidx[c + 3]]);
+      if (r - c >= 0 && r - c < 4) {
+        if (r == c) v.x = dg;
+        if (r == c + 1) v.y = dg;
+        if (r == c + 2) v.z = dg;
+        if (r == c + 3) v.w = dg;
+      }
+      *reinterpret_cast<float4*>(dst + c) = v;
+    }
+  }
+}
+
+// The same gather one element per thread, for d_in beyond the largest staged row.
+__global__ __launch_bounds__(256) void gather_reversed_scalar_kernel(const float* __restrict__ H, int64_t bsh,
+                                                                     const int32_t* __restrict__ perm,
+                                                                     const double* __restrict__ key,
+                                                                     const double* __restrict__ lambda,
+                                                                     int d_in, float* __restrict__ A) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   const int r = blockIdx.y;
   const int e = blockIdx.z;
-  if (c >= d_in) return;
+  if (c >= d_in || c >= (r / NB + 1) * NB) return;
   const int32_t* pe = perm + static_cast<int64_t>(e) * d_in;
-  // indices are clamped so that a malformed permutation can never address outside H
   const int pr = min(max(pe[d_in - 1 - r], 0), d_in - 1);
   const int pc = min(max(pe[d_in - 1 - c], 0), d_in - 1);
-  float v;
-  if (r == c) {
-    v = static_cast<float>(key[static_cast<int64_t>(e) * d_in + pr] + lambda[e]);
-  } else {
-    v = H[static_cast<int64_t>(e) * bsh + static_cast<int64_t>(pr) * d_in + pc];
-  }
+  const float v = (r == c) ? static_cast<float>(key[static_cast<int64_t>(e) * d_in + pr] + lambda[e])
+                           : H[static_cast<int64_t>(e) * bsh + static_cast<int64_t>(pr) * d_in + pc];
   A[(static_cast<int64_t>(e) * d_in + r) * d_in + c] = v;
 }
 
@@ -358,16 +401,26 @@ __global__ __launch_bounds__(256) void potrf_block_kernel(const float* __restric
   }
 }
 
-// U[i][j] = Linv[d-1-i][d-1-j] for j >= i, 0 below the diagonal.
+// U[i][j] = Linv[d-1-i][d-1-j] for j >= i, 0 below the diagonal.  Each thread writes 4
+// consecutive j of REV_ROWS rows (one reversed float4 of the source row each).
+constexpr int REV_ROWS = 8;
 __global__ __launch_bounds__(256) void reverse_to_upper_kernel(const float* __restrict__ Linv, int d_in,
                                                                float* __restrict__ U, int64_t bsu) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  const int i = blockIdx.y;
+  const int j = 4 * (blockIdx.x * 256 + threadIdx.x);
   const int e = blockIdx.z;
   if (j >= d_in) return;
-  float v = 0.0f;
-  if (j >= i) v = Linv[(static_cast<int64_t>(e) * d_in + (d_in - 1 - i)) * d_in + (d_in - 1 - j)];
-  U[static_cast<int64_t>(e) * bsu + static_cast<int64_t>(i) * d_in + j] = v;
+#pragma unroll 2
+  for (int q = 0; q < REV_ROWS; ++q) {
+    const int i = blockIdx.y * REV_ROWS + q;
+    if (i >= d_in) break;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j + 3 >= i) {
+      const float4 s = *reinterpret_cast<const float4*>(
+          Linv + (static_cast<int64_t>(e) * d_in + (d_in - 1 - i)) * d_in + (d_in - 4 - j));
+      v = make_float4(j >= i ? s.w : 0.0f, j + 1 >= i ? s.z : 0.0f, j + 2 >= i ? s.y : 0.0f, s.x);
+    }
+    *reinterpret_cast<float4*>(U + static_cast<int64_t>(e) * bsu + static_cast<int64_t>(i) * d_in + j) = v;
+  }
 }
 
 // Floats of T per problem for trtri_doubling: the largest level, (full groups + 1) h^2.
@@ -537,8 +590,24 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
   GPTQ_LAUNCH(perm_scatter_kernel, dim3(cb, batch), blk, 0, stream, w.rank, d_in, p.act_order, perm);
   GPTQ_LAUNCH(damping_kernel, dim3(batch), blk, 0, stream, w.key, d_in, static_cast<double>(p.damp),
               w.lambda, w.flag);
-  GPTQ_LAUNCH(gather_reversed_kernel, dim3(cb, d_in, batch), blk, 0, stream, H, bsh, perm, w.key,
-              w.lambda, d_in, w.A);
+  {
+    const bool vec = reinterpret_cast<uintptr_t>(H) % 16 == 0 && (batch == 1 || bsh % 4 == 0);
+    const dim3 gg((d_in + GATHER_ROWS - 1) / GATHER_ROWS, batch);
+#define GPTQ_GATHER(DMAX)                                                                                   \
+  do {                                                                                                     \
+    if (vec) GPTQ_LAUNCH((gather_reversed_kernel<DMAX, true>), gg, blk, 0, stream, H, bsh, perm, w.key, w.lambda, \
+                         d_in, w.A);                                                                       \
+    else GPTQ_LAUNCH((gather_reversed_kernel<DMAX, false>), gg, blk, 0, stream, H, bsh, perm, w.key, w.lambda,    \
+                     d_in, w.A);                                                                           \
+  } while (0)
+    if (d_in <= 2048) GPTQ_GATHER(2048);
+    else if (d_in <= 4096) GPTQ_GATHER(4096);
+    else if (d_in <= 8192) GPTQ_GATHER(8192);
+    else if (d_in <= 16384) GPTQ_GATHER(16384);
+    else GPTQ_LAUNCH(gather_reversed_scalar_kernel, dim3(cb, d_in, batch), blk, 0, stream, H, bsh, perm, w.key,
+                     w.lambda, d_in, w.A);
+#undef GPTQ_GATHER
+  }
   // L is built in the U buffer (same shape), then replaced by U at the end.
   {
     std::lock_guard<std::mutex> lk(side_mutex());
@@ -548,7 +617,8 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
     if ((st = chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc)) != GPTQ_OK) return st;
     if ((st = trtri_doubling(d_in, U, bsu, w.Linv, w.T, d_in / NB, batch, stream)) != GPTQ_OK) return st;
   }
-  GPTQ_LAUNCH(reverse_to_upper_kernel, dim3(cb, d_in, batch), blk, 0, stream, w.Linv, d_in, U, bsu);
+  GPTQ_LAUNCH(reverse_to_upper_kernel, dim3((d_in / 4 + 255) / 256, (d_in + REV_ROWS - 1) / REV_ROWS, batch), blk, 0,
+              stream, w.Linv, d_in, U, bsu);
 
   // read back the per-problem pivot flags
   int any = 0;

@@ -19,6 +19,7 @@
 //     lazy update:   hierarchical (see sweep_range): W_p[:, right] -= Err[:, left] @ U[left,
 //                    right] on the fp32 matrix cores, Err [d_out, d_in] in processing order.
 //   unpermute:       codes back to original column order; g_idx.
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -26,6 +27,67 @@
 namespace gptq {
 namespace {
 
+// Rows and index tables are staged in LDS: the per-problem table (source column, or a
+// sentinel for dead columns) once per workgroup, then each row of W read in 16-byte vectors
+// and gathered from LDS into float4 stores.  kVec: W rows are 16-byte aligned.
+constexpr int STAGE_ROWS = 8;       // rows per workgroup of the staged permutes
+constexpr int kStagedMax = 16384;   // largest d_in whose row and index table are staged
+constexpr uint16_t kDeadCol = 0xFFFF;
+template <typename T, int DMAX, bool kVec>
+__global__ __launch_bounds__(256) void permute_weight_staged_kernel(const T* __restrict__ W, int64_t ldw,
+                                                                    int64_t bsw, const int32_t* __restrict__ perm,
+                                                                    const uint8_t* __restrict__ dead, int d_out,
+                                                                    int d_in, float* __restrict__ Wp) {
+  __shared__ __attribute__((aligned(16))) float srow[DMAX];
+  __shared__ uint16_t sidx[DMAX];
+  const int e = blockIdx.y, t = threadIdx.x;
+  for (int j = t; j < d_in; j += 256) {
+    // a malformed permutation is clamped into range rather than addressing outside W
+    const int c = min(max(perm[static_cast<int64_t>(e) * d_in + j], 0), d_in - 1);
+    sidx[j] = dead[static_cast<int64_t>(e) * d_in + c] ? kDeadCol : static_cast<uint16_t>(c);
+  }
+  for (int i = 0; i < STAGE_ROWS; ++i) {
+    const int r = blockIdx.x * STAGE_ROWS + i;
+    if (r >= d_out) break;
+    __syncthreads();  // sidx written / the previous row fully consumed
+    const T* src = W + static_cast<int64_t>(e) * bsw + static_cast<int64_t>(r) * ldw;
+    if constexpr (kVec && sizeof(T) == 2) {
+      for (int c8 = t; c8 < d_in / 8; c8 += 256) {
+        const uint4 v = reinterpret_cast<const uint4*>(src)[c8];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          T lo, hi;
+          lo.bits = static_cast<uint16_t>(u[q] & 0xFFFFu);
+          hi.bits = static_cast<uint16_t>(u[q] >> 16);
+          f[2 * q] = load_as_f32(&lo);
+          f[2 * q + 1] = load_as_f32(&hi);
+        }
+        reinterpret_cast<float4*>(srow)[2 * c8] = make_float4(f[0], f[1], f[2], f[3]);
+        reinterpret_cast<float4*>(srow)[2 * c8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    } else if constexpr (kVec) {
+      for (int c4 = t; c4 < d_in / 4; c4 += 256)
+        reinterpret_cast<float4*>(srow)[c4] = reinterpret_cast<const float4*>(src)[c4];
+    } else {
+      for (int c = t; c < d_in; c += 256) srow[c] = load_as_f32(src + c);
+    }
+    __syncthreads();
+    float* dst = Wp + (static_cast<int64_t>(e) * d_out + r) * d_in;
+    for (int j = 4 * t; j < d_in; j += 1024) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint16_t c = sidx[j + q];
+        v[q] = c == kDeadCol ? 0.0f : srow[c];
+      }
+      *reinterpret_cast<float4*>(dst + j) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// One element per thread, for d_in beyond the largest staged row.
 template <typename T>
 __global__ __launch_bounds__(256) void permute_weight_kernel(const T* __restrict__ W, int64_t ldw, int64_t bsw,
                                                              const int32_t* __restrict__ perm,
@@ -234,6 +296,48 @@ __global__ __launch_bounds__(256) void block_sweep_kernel(const float* __restric
   for (int m = 0; m < 8; ++m) edst[16 * m + k] = w[m];
 }
 
+// codes[:, c] = codes_p[:, inv[c]]; g_idx[c] = inv[c] / group.  Staged like the weight
+// permute: inv once per workgroup, each codes_p row in LDS, 16 codes per thread per store.
+// kVec: the codes rows are 16-byte aligned.
+template <int DMAX, bool kVec>
+__global__ __launch_bounds__(256) void unpermute_staged_kernel(const uint8_t* __restrict__ codes_p,
+                                                               const int32_t* __restrict__ inv, int d_out,
+                                                               int d_in, int group, uint8_t* __restrict__ codes,
+                                                               int32_t* __restrict__ g_idx) {
+  __shared__ __attribute__((aligned(16))) uint8_t srow[DMAX];
+  __shared__ uint16_t sidx[DMAX];
+  const int e = blockIdx.y, t = threadIdx.x;
+  for (int c = t; c < d_in; c += 256) {
+    const int j = min(max(inv[static_cast<int64_t>(e) * d_in + c], 0), d_in - 1);
+    sidx[c] = static_cast<uint16_t>(j);
+    if (blockIdx.x == 0) g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? j / group : 0;
+  }
+  for (int i = 0; i < STAGE_ROWS; ++i) {
+    const int r = blockIdx.x * STAGE_ROWS + i;
+    if (r >= d_out) break;
+    __syncthreads();
+    const int64_t ro = (static_cast<int64_t>(e) * d_out + r) * d_in;
+    // codes_p rows start at multiples of d_in (a multiple of 128) in a 256-byte aligned workspace
+    for (int c16 = t; c16 < d_in / 16; c16 += 256)
+      reinterpret_cast<uint4*>(srow)[c16] = reinterpret_cast<const uint4*>(codes_p + ro)[c16];
+    __syncthreads();
+    if constexpr (kVec) {
+      for (int c = 16 * t; c < d_in; c += 4096) {
+        uint32_t u[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          u[q] = static_cast<uint32_t>(srow[sidx[c + 4 * q]]) | (static_cast<uint32_t>(srow[sidx[c + 4 * q + 1]]) << 8) |
+                 (static_cast<uint32_t>(srow[sidx[c + 4 * q + 2]]) << 16) |
+                 (static_cast<uint32_t>(srow[sidx[c + 4 * q + 3]]) << 24);
+        *reinterpret_cast<uint4*>(codes + ro + c) = make_uint4(u[0], u[1], u[2], u[3]);
+      }
+    } else {
+      for (int c = t; c < d_in; c += 256) codes[ro + c] = srow[sidx[c]];
+    }
+  }
+}
+
+// One element per thread, for d_in beyond the largest staged row.
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p,
                                                         const int32_t* __restrict__ inv, int d_out, int d_in,
                                                         int group, uint8_t* __restrict__ codes,
@@ -330,19 +434,51 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
   const dim3 blk(256);
   const int cb = (d_in + 255) / 256;
   const dim3 pg(cb, d_out, batch);
-  switch (w_dtype) {
-    case GPTQ_F32:
-      GPTQ_LAUNCH(permute_weight_kernel<float>, pg, blk, 0, stream, static_cast<const float*>(W), ldw, bsw, perm,
-                  dead, d_out, d_in, w.Wp);
-      break;
-    case GPTQ_BF16:
-      GPTQ_LAUNCH(permute_weight_kernel<BF16>, pg, blk, 0, stream, static_cast<const BF16*>(W), ldw, bsw, perm,
-                  dead, d_out, d_in, w.Wp);
-      break;
-    case GPTQ_F16:
-      GPTQ_LAUNCH(permute_weight_kernel<F16>, pg, blk, 0, stream, static_cast<const F16*>(W), ldw, bsw, perm,
-                  dead, d_out, d_in, w.Wp);
-      break;
+  const dim3 sgr((d_out + STAGE_ROWS - 1) / STAGE_ROWS, batch);
+  {
+    const size_t tb = w_dtype == GPTQ_F32 ? 4 : 2;
+    const bool vec = reinterpret_cast<uintptr_t>(W) % 16 == 0 && (ldw * tb) % 16 == 0 &&
+                     (batch == 1 || (bsw * tb) % 16 == 0);
+    gptq_status st = GPTQ_OK;
+    auto staged = [&](auto tag, auto dmax) {
+      using T = decltype(tag);
+      constexpr int DM = decltype(dmax)::value;
+      const T* Wt = static_cast<const T*>(W);
+      if (vec) GPTQ_LAUNCH((permute_weight_staged_kernel<T, DM, true>), sgr, blk, 0, stream, Wt, ldw, bsw, perm, dead,
+                           d_out, d_in, w.Wp);
+      else GPTQ_LAUNCH((permute_weight_staged_kernel<T, DM, false>), sgr, blk, 0, stream, Wt, ldw, bsw, perm, dead,
+                       d_out, d_in, w.Wp);
+      return GPTQ_OK;
+    };
+    auto by_dtype = [&](auto dmax) {
+      switch (w_dtype) {
+        case GPTQ_F32: return staged(float{}, dmax);
+        case GPTQ_BF16: return staged(BF16{}, dmax);
+        case GPTQ_F16: return staged(F16{}, dmax);
+      }
+      return GPTQ_ERR_INVALID_ARG;
+    };
+    if (d_in <= 2048) st = by_dtype(std::integral_constant<int, 2048>{});
+    else if (d_in <= 4096) st = by_dtype(std::integral_constant<int, 4096>{});
+    else if (d_in <= 8192) st = by_dtype(std::integral_constant<int, 8192>{});
+    else if (d_in <= kStagedMax) st = by_dtype(std::integral_constant<int, kStagedMax>{});
+    else {
+      switch (w_dtype) {
+        case GPTQ_F32:
+          GPTQ_LAUNCH(permute_weight_kernel<float>, pg, blk, 0, stream, static_cast<const float*>(W), ldw, bsw, perm,
+                      dead, d_out, d_in, w.Wp);
+          break;
+        case GPTQ_BF16:
+          GPTQ_LAUNCH(permute_weight_kernel<BF16>, pg, blk, 0, stream, static_cast<const BF16*>(W), ldw, bsw, perm,
+                      dead, d_out, d_in, w.Wp);
+          break;
+        case GPTQ_F16:
+          GPTQ_LAUNCH(permute_weight_kernel<F16>, pg, blk, 0, stream, static_cast<const F16*>(W), ldw, bsw, perm,
+                      dead, d_out, d_in, w.Wp);
+          break;
+      }
+    }
+    if (st != GPTQ_OK) return st;
   }
   GPTQ_LAUNCH(inverse_perm_kernel, dim3(cb, batch), blk, 0, stream, perm, d_in, w.inv);
   if (G == 0) {
@@ -352,7 +488,22 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
   const gptq_status st = sweep_range(0, d_in / kBlock, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales,
                                      zeros);
   if (st != GPTQ_OK) return st;
-  GPTQ_LAUNCH(unpermute_kernel, pg, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G, codes, g_idx);
+  {
+    const bool vec = reinterpret_cast<uintptr_t>(codes) % 16 == 0;
+    auto staged = [&](auto dmax) {
+      constexpr int DM = decltype(dmax)::value;
+      if (vec) GPTQ_LAUNCH((unpermute_staged_kernel<DM, true>), sgr, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G,
+                           codes, g_idx);
+      else GPTQ_LAUNCH((unpermute_staged_kernel<DM, false>), sgr, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G,
+                       codes, g_idx);
+      return GPTQ_OK;
+    };
+    gptq_status st = GPTQ_OK;
+    if (d_in <= 4096) st = staged(std::integral_constant<int, 4096>{});
+    else if (d_in <= kStagedMax) st = staged(std::integral_constant<int, kStagedMax>{});
+    else GPTQ_LAUNCH(unpermute_kernel, pg, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G, codes, g_idx);
+    if (st != GPTQ_OK) return st;
+  }
   return GPTQ_OK;
 }
 
