@@ -142,26 +142,41 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
   }
 }
 
-// DPP within a row of 16 lanes: broadcast of lane `src`, and rotation by `n`.
-template <int src>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + src, 0xF, 0xF, false));
+// A row of W is spread over LPR lanes (16: one DPP row; 4: one DPP quad).  Broadcast of
+// lane `src` of the group, and min / max over the group.
+template <int LPR, int src>
+__device__ __forceinline__ float grp_bcast(float v) {
+  if constexpr (LPR == 16) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + src, 0xF, 0xF, false));
+  else return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), src * 0x55, 0xF, 0xF, false));
 }
-template <int n>
-__device__ __forceinline__ float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + n, 0xF, 0xF, false));
+template <int ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row_min(float v) {
-  v = fminf(v, row_ror<8>(v));
-  v = fminf(v, row_ror<4>(v));
-  v = fminf(v, row_ror<2>(v));
-  return fminf(v, row_ror<1>(v));
+// row_ror:n = 0x120 + n; quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E
+template <int LPR>
+__device__ __forceinline__ float grp_min(float v) {
+  if constexpr (LPR == 16) {
+    v = fminf(v, dpp_f<0x128>(v));
+    v = fminf(v, dpp_f<0x124>(v));
+    v = fminf(v, dpp_f<0x122>(v));
+    return fminf(v, dpp_f<0x121>(v));
+  } else {
+    v = fminf(v, dpp_f<0xB1>(v));
+    return fminf(v, dpp_f<0x4E>(v));
+  }
 }
-__device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, row_ror<8>(v));
-  v = fmaxf(v, row_ror<4>(v));
-  v = fmaxf(v, row_ror<2>(v));
-  return fmaxf(v, row_ror<1>(v));
+template <int LPR>
+__device__ __forceinline__ float grp_max(float v) {
+  if constexpr (LPR == 16) {
+    v = fmaxf(v, dpp_f<0x128>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x122>(v));
+    return fmaxf(v, dpp_f<0x121>(v));
+  } else {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    return fmaxf(v, dpp_f<0x4E>(v));
+  }
 }
 
 template <int... I, typename F>
@@ -169,61 +184,71 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
   (f(std::integral_constant<int, I>{}), ...);
 }
 
-constexpr int SW_ROWS = 16;   // rows of W per workgroup: 16 lanes per row, 4 rows per wave
-
 // One 128-column block of the sweep.  G = group size (16, 32, 64 or 128), or 0 for the
-// per-row grid already written by row_grid_kernel.
+// per-row grid already written by row_grid_kernel.  NT threads per workgroup, LPR lanes
+// per row of W, so NT / LPR rows per workgroup.
 //
-// A row of W is spread over one DPP row of 16 lanes: lane k keeps columns 16m + k
-// (m = 0..7) in registers.  For column j the owner lane's value is broadcast to the row
-// (row_newbcast), every lane of the row quantizes it (so all 16 hold err_j and code_j),
-// and each lane updates its own later columns.  The U block sits in LDS as
-// Ul[j][8k + m] = U[j0 + j][j0 + 16m + k] with its diagonal zeroed (1/U_jj kept apart):
-// a lane's update reads are contiguous, the four rows of a wave read the same words, and
+// Lane k of a row keeps the C = 128 / LPR columns LPR m + k (m = 0..C-1) in registers.
+// For column j the owner lane's value is broadcast to the row's lanes, every lane of the
+// row quantizes it (so all hold err_j and code_j), and each lane updates its own later
+// columns: with the columns interleaved every lane has the same number of them, so the
+// update loop starts at a compile-time index.  Fewer lanes per row repeat the per-column
+// quantization on fewer lanes (4 lanes: a quarter of the instructions per row and column
+// of 16), but need 4x the rows to fill the chip.  The U block sits in LDS as
+// Ul[j][CP k + m] = U[j0 + j][j0 + LPR m + k] with its diagonal zeroed (1/U_jj kept apart):
+// a lane's update reads are contiguous, the rows of a wave read the same words, and
 // columns at or before j get a zero factor.  At a group start the grid is fitted on the
-// row's current values of the group's columns (min/max reduced over the 16 lanes).
-template <int G>
-__global__ __launch_bounds__(256) void block_sweep_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
-                                                          int64_t bsu, int d_out, int d_in, int blk, float maxq,
-                                                          float* __restrict__ scales, uint8_t* __restrict__ zeros,
-                                                          uint8_t* __restrict__ codes_p, float* __restrict__ err) {
-  __shared__ __attribute__((aligned(16))) float Ul[kBlock * kBlock];
+// row's current values of the group's columns (min/max reduced over the row's lanes).
+template <int G, int NT, int LPR>
+__global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
+                                                         int64_t bsu, int d_out, int d_in, int blk, float maxq,
+                                                         float* __restrict__ scales, uint8_t* __restrict__ zeros,
+                                                         uint8_t* __restrict__ codes_p, float* __restrict__ err) {
+  constexpr int C = kBlock / LPR;   // columns per lane
+  constexpr int CW = C / 4;         // code words per lane
+  constexpr int CQ = C / 4;         // float4 of a U row per lane
+  // a lane's slice of a U row in LDS: padded at 4 lanes per row, so that the four lanes'
+  // 16-byte reads start on different banks (unpadded, 32 floats apart, they collide)
+  constexpr int CP = LPR == 4 ? C + 4 : C;
+  constexpr int UR = LPR * CP;      // floats per staged U row
+  static_assert(G == 0 || G % LPR == 0, "a group spans whole registers");
+  __shared__ __attribute__((aligned(16))) float Ul[kBlock * UR];
   __shared__ float inv_d[kBlock];
   const int e = blockIdx.y;
   const int tid = threadIdx.x;
   const int j0 = blk * kBlock;
   const float* Ub = U + static_cast<int64_t>(e) * bsu + static_cast<int64_t>(j0) * d_in + j0;
-  const int r = blockIdx.x * SW_ROWS + (tid >> 4);
-  const int k = tid & 15;
+  const int r = blockIdx.x * (NT / LPR) + tid / LPR;
+  const int k = tid % LPR;
   const bool live = r < d_out;
   // the row's block columns are fetched first, so they arrive while U is staged
   const float* wrow = Wp + (static_cast<int64_t>(e) * d_out + (live ? r : 0)) * d_in + j0;
-  float w[8];
+  float w[C];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) w[m] = wrow[16 * m + k];
-  // stage the U block: thread (row j, lane kk) gathers U[j][16m + kk], m = 0..7 (each load
-  // instruction reads 16 consecutive floats across the lanes) and writes them as 8
+  for (int m = 0; m < C; ++m) w[m] = wrow[LPR * m + k];
+  // stage the U block: thread (row j, lane kk) gathers U[j][LPR m + kk], m = 0..C-1 (each
+  // load instruction reads LPR consecutive floats per row) and writes them as C
   // consecutive floats
-#pragma unroll 2
-  for (int i = tid; i < kBlock * 16; i += 256) {
-    const int j = i >> 4, kk = i & 15;
+#pragma unroll 1
+  for (int i = tid; i < kBlock * LPR; i += NT) {
+    const int j = i / LPR, kk = i % LPR;
     const float* src = Ub + static_cast<int64_t>(j) * d_in + kk;
-    float v[8];
+    float v[C];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) v[m] = src[16 * m];
+    for (int m = 0; m < C; ++m) v[m] = src[LPR * m];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (16 * m + kk == j) {
+    for (int m = 0; m < C; ++m) {
+      if (LPR * m + kk == j) {
         inv_d[j] = 1.0f / v[m];
         v[m] = 0.0f;
       }
     }
-    float4* dst = reinterpret_cast<float4*>(Ul + j * kBlock + 8 * kk);
-    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    float4* dst = reinterpret_cast<float4*>(Ul + j * UR + CP * kk);
+#pragma unroll
+    for (int q = 0; q < CQ; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
   __syncthreads();
-  if (!live) return;   // whole rows of 16 lanes leave together; no barrier follows
+  if (!live) return;   // whole rows leave together; no barrier follows
   const int n_groups = G ? d_in / G : 1;
   float* sc = scales + static_cast<int64_t>(e) * n_groups * d_out;
   uint8_t* zr = zeros + static_cast<int64_t>(e) * n_groups * d_out;
@@ -233,27 +258,30 @@ __global__ __launch_bounds__(256) void block_sweep_kernel(const float* __restric
     z = static_cast<float>(zr[r]);
     inv_s = 1.0f / s;
   }
-  // lane k stores the codes of columns 8k..8k+7 (two words)
-  uint32_t cw0 = 0u, cw1 = 0u;
-  const float* ul_k = Ul + 8 * k;
+  // lane k stores the codes of columns C k .. C k + C - 1
+  uint32_t cw[CW];
+#pragma unroll
+  for (int q = 0; q < CW; ++q) cw[q] = 0u;
+  const float* ul_k = Ul + CP * k;
   // U row j is read into registers one column ahead (two alternating sets), so that the
   // LDS latency stays off the column-to-column chain
-  float4 ua0 = *reinterpret_cast<const float4*>(ul_k), ua1 = *reinterpret_cast<const float4*>(ul_k + 4);
-  float4 ub0, ub1;
+  float4 ua[CQ], ub[CQ];
+#pragma unroll
+  for (int q = 0; q < CQ; ++q) ua[q] = reinterpret_cast<const float4*>(ul_k)[q];
   float dja = inv_d[0], djb = 0.0f;
 
   static_for(std::make_integer_sequence<int, kBlock>{}, [&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    constexpr int mj = j >> 4;
-    float4& cur0 = (j & 1) ? ub0 : ua0;
-    float4& cur1 = (j & 1) ? ub1 : ua1;
-    float4& nxt0 = (j & 1) ? ua0 : ub0;
-    float4& nxt1 = (j & 1) ? ua1 : ub1;
+    constexpr int mj = j / LPR;
+    float4* cur = (j & 1) ? ub : ua;
+    float4* nxt = (j & 1) ? ua : ub;
     const float dj = (j & 1) ? djb : dja;
     if constexpr (j + 1 < kBlock) {
-      const float* un = ul_k + (j + 1) * kBlock;
-      if constexpr (((j + 1) >> 4) < 4) nxt0 = *reinterpret_cast<const float4*>(un);
-      nxt1 = *reinterpret_cast<const float4*>(un + 4);
+      const float4* un = reinterpret_cast<const float4*>(ul_k + (j + 1) * UR);
+      static_for(std::make_integer_sequence<int, CQ>{}, [&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (4 * q + 3 >= (j + 1) / LPR) nxt[q] = un[q];
+      });
       if constexpr (j & 1) dja = inv_d[j + 1];
       else djb = inv_d[j + 1];
       // the scheduler would sink these reads next to their use in the next column
@@ -262,12 +290,12 @@ __global__ __launch_bounds__(256) void block_sweep_kernel(const float* __restric
     if constexpr (G != 0 && j % G == 0) {
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-      for (int m = j / 16; m < (j + G) / 16; ++m) {
+      for (int m = j / LPR; m < (j + G) / LPR; ++m) {
         lo = fminf(lo, w[m]);
         hi = fmaxf(hi, w[m]);
       }
-      lo = row_min(lo);
-      hi = row_max(hi);
+      lo = grp_min<LPR>(lo);
+      hi = grp_max<LPR>(hi);
       s = fmaxf((hi - lo) / maxq, 1e-8f);
       z = rintf(-lo / s);
       inv_s = 1.0f / s;
@@ -277,23 +305,29 @@ __global__ __launch_bounds__(256) void block_sweep_kernel(const float* __restric
         zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
       }
     }
-    const float wj = row_bcast<j & 15>(w[mj]);
+    const float wj = grp_bcast<LPR, j % LPR>(w[mj]);
     const float q = fminf(fmaxf(rintf(wj * inv_s) + z, 0.0f), maxq);
     const float wq = s * (q - z);
     const float e_j = (wj - wq) * dj;
-    const uint32_t qb = (k == (j >> 3)) ? (static_cast<uint32_t>(q) << (8 * (j & 3))) : 0u;
-    if constexpr ((j & 4) == 0) cw0 |= qb;
-    else cw1 |= qb;
-    const float u[8] = {cur0.x, cur0.y, cur0.z, cur0.w, cur1.x, cur1.y, cur1.z, cur1.w};
+    cw[(j % C) / 4] |= (k == j / C) ? (static_cast<uint32_t>(q) << (8 * (j & 3))) : 0u;
 #pragma unroll
-    for (int m = mj; m < 8; ++m) w[m] = fmaf(-e_j, u[m], w[m]);
-    if (k == (j & 15)) w[mj] = e_j;   // the owner keeps err_j in place of w_j
+    for (int m = mj; m < C; ++m) {
+      const float4 u4 = cur[m / 4];
+      const float u = (m & 3) == 0 ? u4.x : (m & 3) == 1 ? u4.y : (m & 3) == 2 ? u4.z : u4.w;
+      w[m] = fmaf(-e_j, u, w[m]);
+    }
+    if (k == j % LPR) w[mj] = e_j;   // the owner keeps err_j in place of w_j
   });
-  uint2* cdst = reinterpret_cast<uint2*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0);
-  cdst[k] = make_uint2(cw0, cw1);
+  uint32_t* cdst = reinterpret_cast<uint32_t*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0 + C * k);
+  if constexpr (CW == 2) {
+    *reinterpret_cast<uint2*>(cdst) = make_uint2(cw[0], cw[1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < CW; q += 4) *reinterpret_cast<uint4*>(cdst + q) = make_uint4(cw[q], cw[q + 1], cw[q + 2], cw[q + 3]);
+  }
   float* edst = err + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) edst[16 * m + k] = w[m];
+  for (int m = 0; m < C; ++m) edst[LPR * m + k] = w[m];
 }
 
 // codes[:, c] = codes_p[:, inv[c]]; g_idx[c] = inv[c] / group.  Staged like the weight
@@ -372,23 +406,79 @@ QuantWs carve(void* ws, int batch, int d_out, int d_in) {
   return w;
 }
 
-template <int G>
+// Launch geometry of the sweep: NT threads per workgroup, LPR lanes per row, the grid.
+struct SweepShape {
+  int nt, lpr;
+  dim3 grid;
+};
+
+// The U block takes 64 KB of LDS, so at most two workgroups share a CU.  With rows enough
+// for about one wave per SIMD at 4 lanes per row (16 rows per wave), rows get 4 lanes;
+// else 16.  Then the largest workgroup that still gives every CU at least one (at most
+// 512 threads for groups of 64 at 4 lanes per row, whose registers would not fit 1024).  The small
+// groups (16, 32) keep 16 lanes and 256 threads: their sweeps need too many registers
+// for more than one wave per SIMD.
+SweepShape sweep_shape(int G, int batch, int d_out) {
+  const bool wide_ok = G == 0 || G == 64 || G == 128;
+  const int64_t rows = static_cast<int64_t>(batch) * d_out;
+  const int lpr = (wide_ok && rows / 16 >= 768) ? 4 : 16;
+  int nt = 256;
+  if (wide_ok) {
+    for (int cand : {1024, 512}) {
+      if (cand == 1024 && lpr == 4 && G == 64) continue;   // would spill registers
+      const int rpw = cand / lpr;
+      if (static_cast<int64_t>((d_out + rpw - 1) / rpw) * batch >= 256) {
+        nt = cand;
+        break;
+      }
+    }
+  }
+  const int rpw = nt / lpr;
+  return {nt, lpr, dim3((d_out + rpw - 1) / rpw, batch)};
+}
+
+template <int G, int NT, int LPR>
 gptq_status launch_sweep(dim3 grid, hipStream_t stream, const float* Wp, const float* U, int64_t bsu, int d_out,
                          int d_in, int blk, float maxq, float* scales, uint8_t* zeros, uint8_t* codes_p,
                          float* err) {
-  GPTQ_LAUNCH(block_sweep_kernel<G>, grid, dim3(256), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales,
-              zeros, codes_p, err);
+  GPTQ_LAUNCH((block_sweep_kernel<G, NT, LPR>), grid, dim3(NT), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq,
+              scales, zeros, codes_p, err);
   return GPTQ_OK;
 }
 
-gptq_status sweep_block(int b, int G, dim3 sg, hipStream_t stream, int d_out, int d_in, const QuantWs& w,
-                        const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
+template <int G>
+gptq_status launch_sweep_nt(const SweepShape& sh, hipStream_t stream, const float* Wp, const float* U, int64_t bsu,
+                            int d_out, int d_in, int blk, float maxq, float* scales, uint8_t* zeros,
+                            uint8_t* codes_p, float* err) {
+  if constexpr (G == 0 || G == 64 || G == 128) {
+#define GPTQ_SWEEP(NT, LPR)                                                                                    \
+  if (sh.nt == NT && sh.lpr == LPR)                                                                           \
+    return launch_sweep<G, NT, LPR>(sh.grid, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales, zeros, codes_p, \
+                                    err);
+    GPTQ_SWEEP(512, 16)   // 1024 threads at 16 lanes: never chosen (4 lanes take over first)
+    if constexpr (G != 64) {
+      GPTQ_SWEEP(1024, 4)
+    }
+    GPTQ_SWEEP(512, 4)
+    GPTQ_SWEEP(256, 4)
+#undef GPTQ_SWEEP
+  }
+  if (sh.nt != 256 || sh.lpr != 16) return GPTQ_ERR_UNSUPPORTED;
+  return launch_sweep<G, 256, 16>(sh.grid, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales, zeros, codes_p, err);
+}
+
+gptq_status sweep_block(int b, int G, const SweepShape& sg, hipStream_t stream, int d_out, int d_in,
+                        const QuantWs& w, const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
   switch (G) {
-    case 0: return launch_sweep<0>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 16: return launch_sweep<16>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 32: return launch_sweep<32>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 64: return launch_sweep<64>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 128: return launch_sweep<128>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 0: return launch_sweep_nt<0>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 16:
+      return launch_sweep_nt<16>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 32:
+      return launch_sweep_nt<32>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 64:
+      return launch_sweep_nt<64>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 128:
+      return launch_sweep_nt<128>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
     default: return GPTQ_ERR_UNSUPPORTED;
   }
 }
@@ -400,7 +490,7 @@ gptq_status sweep_block(int b, int G, dim3 sg, hipStream_t stream, int d_out, in
 // split, after j's error is known and before k is quantized, so the updates are the same
 // as applying each block's errors to all later columns right after the block; only the
 // time at which they land changes.  Most of the flops move into a few large products.
-gptq_status sweep_range(int b0, int b1, int G, dim3 sg, hipStream_t stream, int batch, int d_out, int d_in,
+gptq_status sweep_range(int b0, int b1, int G, const SweepShape& sg, hipStream_t stream, int batch, int d_out, int d_in,
                         const QuantWs& w, const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
   if (b1 - b0 == 1) return sweep_block(b0, G, sg, stream, d_out, d_in, w, U, bsu, maxq, scales, zeros);
   const int bm = b0 + (b1 - b0) / 2;
@@ -484,7 +574,7 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
   if (G == 0) {
     GPTQ_LAUNCH(row_grid_kernel, dim3(d_out, batch), blk, 0, stream, w.Wp, d_out, d_in, maxq, scales, zeros);
   }
-  const dim3 sg((d_out + SW_ROWS - 1) / SW_ROWS, batch);
+  const SweepShape sg = sweep_shape(G, batch, d_out);
   const gptq_status st = sweep_range(0, d_in / kBlock, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales,
                                      zeros);
   if (st != GPTQ_OK) return st;

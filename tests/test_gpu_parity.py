@@ -38,6 +38,15 @@ CASES = {
                                           act_order=True),
     "two_bit": synth.scaled("mlp_down", d_out=64, d_in=256, n_tokens=800, seq_len=800, bits=2),
     "eight_bit": synth.scaled("attn_proj", d_out=64, d_in=256, n_tokens=800, seq_len=800, bits=8),
+    # rows enough for the other sweep shapes (threads per workgroup, lanes per row):
+    # 256 / 4, 512 / 16, 256 / 4 per row, 512 / 4
+    "group64_many_rows": synth.scaled("moe", d_out=512, d_in=256, n_tokens=600, batch=32, seq_len=300,
+                                      group_size=64),
+    "per_row_many_rows": synth.scaled("moe", d_out=520, d_in=256, n_tokens=600, batch=16, seq_len=300,
+                                      group_size=-1),
+    "per_row_4_lanes": synth.scaled("moe", d_out=520, d_in=256, n_tokens=600, batch=24, seq_len=300,
+                                    group_size=-1),
+    "group128_4_lanes_512": synth.scaled("moe", d_out=512, d_in=128, n_tokens=400, batch=64, seq_len=200),
 }
 
 
