@@ -32,7 +32,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int GPB = kTransB ? GT + 1 : GT + 4;
   constexpr int MB = TT / 64;
   constexpr int RQ = GT * GK / 1024;  // float4 loads per thread per operand and stage
-  const int n0 = blockIdx.x * GT, m0 = blockIdx.y * GT;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id, so with 8 column tiles
+  // per row XCD c would get every tile of column c.  Triangular operands and lower-only
+  // outputs make the work of a tile depend on its column, so the column index is rotated
+  // by the row and batch index: every XCD gets a mix of columns.
+  const int bx = static_cast<int>((blockIdx.x + blockIdx.y + blockIdx.z) % gridDim.x);
+  const int n0 = bx * GT, m0 = blockIdx.y * GT;
   if ((g.flags & kLowerOut) && n0 > m0) return;
   const int zo = blockIdx.z / g.batch2, zi = blockIdx.z % g.batch2;
   const float* A = g.A + static_cast<int64_t>(zo) * g.sA + static_cast<int64_t>(zi) * g.sA2;

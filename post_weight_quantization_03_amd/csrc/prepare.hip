@@ -470,6 +470,9 @@ PrepWs carve(void* ws, int batch, int d_in) {
 // far(k) starts once panel(k) is done; near(k+1) writes block column k+2, which far(k)
 // also writes, so it waits for far(k).  Every block receives the updates of all earlier
 // panels before it is factored: the last one from near, the others from far.
+// From this many problems per call on, the Cholesky runs left-looking on one stream.
+constexpr int kLeftLookingBatch = 4;
+
 struct Sched {
   hipStream_t main;
   SideStream* side;
@@ -478,6 +481,42 @@ struct Sched {
 
 float* block_at(float* base, int d_in, int bi, int bj) {
   return base + static_cast<int64_t>(bi) * NB * d_in + static_cast<int64_t>(bj) * NB;
+}
+
+// Left-looking variant for many problems at once, on one stream: block column k first
+// takes the contributions of all earlier columns in one product,
+//   A[k:, k] -= L[k:, :k] L[k, :k]^T   (K = 128 k),
+// then the leaf factors its diagonal block and the panel solve gives L[k+1:, k].  With a
+// batch of problems every step already fills the chip, and the trailing matrix is not
+// read and written back once per block column as in the right-looking order.
+gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, int nb, int batch,
+                      hipStream_t s0) {
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  for (int k = 0; k < nb; ++k) {
+    gptq_status st;
+    if (k > 0) {
+      GemmArgs u{};
+      u.batch = batch;
+      u.M = (nb - k) * NB; u.N = NB; u.K = k * NB;
+      u.A = block_at(L, d_in, k, 0); u.lda = d_in; u.sA = bsl;
+      u.B = u.A; u.ldb = d_in; u.sB = bsl;                         // block row k of L
+      u.C = block_at(A, d_in, k, k); u.ldc = d_in; u.sC = dd;
+      u.alpha = -1.0f; u.beta = 1.0f; u.transB = 1; u.flags = 0;
+      if ((st = gemm_f32(u, s0)) != GPTQ_OK) return st;
+    }
+    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
+    const int rest = nb - k - 1;
+    if (rest == 0) break;
+    GemmArgs g{};
+    g.batch = batch;
+    g.M = rest * NB; g.N = NB; g.K = NB;
+    g.A = block_at(A, d_in, k + 1, k); g.lda = d_in; g.sA = dd;
+    g.B = block_at(Linv, d_in, k, k); g.ldb = d_in; g.sB = dd;
+    g.C = block_at(L, d_in, k + 1, k); g.ldc = d_in; g.sC = bsl;
+    g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower;
+    if ((st = gemm_f32(g, s0)) != GPTQ_OK) return st;
+  }
+  return GPTQ_OK;
 }
 
 gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc) {
@@ -614,7 +653,9 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
     Sched sc{stream, nullptr, d_in / NB, batch};
     gptq_status st = side_stream(&sc.side);
     if (st != GPTQ_OK) return st;
-    if ((st = chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc)) != GPTQ_OK) return st;
+    st = batch >= kLeftLookingBatch ? chol_left(d_in, w.A, U, bsu, w.Linv, w.flag, d_in / NB, batch, stream)
+                                    : chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc);
+    if (st != GPTQ_OK) return st;
     if ((st = trtri_doubling(d_in, U, bsu, w.Linv, w.T, d_in / NB, batch, stream)) != GPTQ_OK) return st;
   }
   GPTQ_LAUNCH(reverse_to_upper_kernel, dim3((d_in / 4 + 255) / 256, (d_in + REV_ROWS - 1) / REV_ROWS, batch), blk, 0,
