@@ -1,19 +1,26 @@
-// fp32 GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32):
+// fp32-accurate GEMM on the gfx950 matrix cores:
 //   C = alpha * op(A) * op(B) + beta * C,   A [M, K], op(B) = B [K, N] or B^T (B [N, K]),
 // batched over blockIdx.z (two nested batch strides).
 //
 // Used for the blocked Cholesky (panel solve as a product with the inverted diagonal
 // block, trailing symmetric update), the triangular inverse, and GPTQ's lazy batch update
 // W[:, later] -= Err @ U[block, later] ("Same Ruler, Smarter Placement: GPTQ", 1.8).
-// Products and sums are fp32, as the quantizer's arithmetic requires; the operands are
-// never rounded to a 16-bit type.
+// Products and sums are fp32, as the quantizer's arithmetic requires.
 //
-// Tile 128 x 128 x 32 (or 64 x 64 x 32 when the grid would be small), 256 threads = 4
-// waves, each owning a quarter of the tile as 32 x 32 MFMA blocks.
-// Operands are staged k-major in LDS so that lanes 0..31 of an MFMA operand read 32
-// consecutive floats.  Triangular operands shrink the K range per tile; a lower-only
-// output skips tiles above the diagonal.
+// Two kernels:
+//  * gemm_x6_kernel, for products that fill the chip with 128 x 128 tiles: the operands
+//    split into three bf16 parts each and six bf16 MFMAs per block (fp32 accuracy at 2.7x
+//    the rate of the fp32 matrix instruction; see the comment at the kernel);
+//  * gemm_f32_kernel (v_mfma_f32_32x32x2_f32), 128 x 128 x 32 tiles for large products
+//    whose shapes are not multiples of 4, and 64 x 64 x 64 tiles for the small products of
+//    the Cholesky chain.
+// Both: 256 threads = 4 waves, each owning a quarter of the tile as 32 x 32 MFMA blocks;
+// triangular operands shrink the K range per tile; a lower-only output skips tiles above
+// the diagonal.
+#include <type_traits>
+
 #include "common.h"
+
 
 namespace gptq {
 namespace {
@@ -202,6 +209,250 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// The same product on the bf16 matrix cores, at fp32 accuracy, by splitting the operands.
+// Each fp32 value is written as x = x0 + x1 + x2 with x0 = bf16(x), x1 = bf16(x - x0),
+// x2 = bf16(x - x0 - x1) (round to nearest even; every difference is exact in fp32), so
+// |x - x0 - x1 - x2| <= 2^-27 |x|.  Of the nine cross products a_i b_j the six with
+// i + j <= 2 are kept; the three dropped ones are below 2^-25 |a b| together.  Products of
+// two bf16 values are exact in fp32 and the sums are fp32, as in the fp32 kernel, so the
+// result carries fp32 rounding: the operands are never rounded to a 16-bit type as a whole.
+// Six v_mfma_f32_32x32x16_bf16 per 32x32x16 block run at 2500 / 6 = 417 TFLOP/s of fp32
+// products against 157 TFLOP/s for v_mfma_f32_32x32x2_f32.
+//
+// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 blocks of 32 x 32), two
+// workgroups per CU.  The three parts are stored in LDS as bf16 planes: A (and B^T) with K
+// contiguous per row, read as 16 bytes per lane (rows 48 bytes apart: a 16-lane read
+// covers all banks once); B [K, N] with N contiguous, read with the transposing
+// ds_read_b64_tr_b16 (k rows 320 bytes apart: a half wave covers all banks once).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+typedef short s16x8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4v lds_s16x4v;
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+
+// parts (x0, x1, x2) of 4 consecutive values, each as 4 packed bf16
+__device__ __forceinline__ void split3(const float4 v, uint2& p0, uint2& p1, uint2& p2) {
+  const uint32_t a0 = pack_bf16(v.x, v.y), b0 = pack_bf16(v.z, v.w);
+  const float rx = v.x - bf16_lo(a0), ry = v.y - bf16_hi(a0), rz = v.z - bf16_lo(b0), rw = v.w - bf16_hi(b0);
+  const uint32_t a1 = pack_bf16(rx, ry), b1 = pack_bf16(rz, rw);
+  const uint32_t a2 = pack_bf16(rx - bf16_lo(a1), ry - bf16_hi(a1)), b2 = pack_bf16(rz - bf16_lo(b1), rw - bf16_hi(b1));
+  p0 = make_uint2(a0, b0);
+  p1 = make_uint2(a1, b1);
+  p2 = make_uint2(a2, b2);
+}
+
+template <bool kTransB>
+__global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
+  constexpr int GT = 128, GK = 16;
+  constexpr int PA = GK + 8;                   // bf16 per K-contiguous row
+  constexpr int PB = GT + 32;                  // bf16 per k row of the N-contiguous layout
+  constexpr int A_PLANE = GT * PA;
+  constexpr int B_PLANE = kTransB ? GT * PA : GK * PB;
+  constexpr int RQ = GT * GK / 1024;           // float4 per thread per operand and stage (2)
+  const int bx = static_cast<int>((blockIdx.x + blockIdx.y + blockIdx.z) % gridDim.x);
+  const int n0 = bx * GT, m0 = blockIdx.y * GT;
+  if ((g.flags & kLowerOut) && n0 > m0) return;
+  const int zo = blockIdx.z / g.batch2, zi = blockIdx.z % g.batch2;
+  const float* A = g.A + static_cast<int64_t>(zo) * g.sA + static_cast<int64_t>(zi) * g.sA2;
+  const float* B = g.B + static_cast<int64_t>(zo) * g.sB + static_cast<int64_t>(zi) * g.sB2;
+  float* C = g.C + static_cast<int64_t>(zo) * g.sC + static_cast<int64_t>(zi) * g.sC2;
+
+  int kb = 0, ke = g.K;
+  if (g.flags & kALower) ke = min(ke, m0 + GT);
+  if (g.flags & kBtLower) ke = min(ke, n0 + GT);
+  if (g.flags & kBLower) kb = max(kb, n0);
+  kb = kb / GK * GK;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][3 * A_PLANE];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][3 * B_PLANE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global loads run two stages ahead through a ring of two register sets (a 16-deep
+  // stage is too short to cover their latency on its own)
+  float4 ra[2][RQ], rb[2][RQ];
+  // Loads are unconditional 16-byte loads from clamped (always valid) addresses; whether
+  // an element is inside the product is applied when the stage is split into LDS.  No
+  // branch or register write touches a load's destination before that, so the loads of a
+  // stage stay in flight until then.  (The host uses this kernel only when K, N and the
+  // leading dimensions are multiples of 4 and the operands 16-byte aligned, so a vector
+  // with k < ke lies entirely inside the K range.)
+  // K-contiguous rows: float4 f = tid + 256 q is (row f / 4, k 4 (f % 4))
+  auto load_rows = [&](const float* P, int64_t ld, int r0, int rlim, int k0, float4* r) {
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int f = tid + 256 * q;
+      const int row = min(r0 + f / 4, rlim - 1), k = min(k0 + 4 * (f % 4), ke - 4);
+      r[q] = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(row) * ld + k);
+    }
+  };
+  auto store_rows = [&](uint16_t* s, const float4* r, int r0, int rlim, int k0) {
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int f = tid + 256 * q;
+      const bool in = (r0 + f / 4 < rlim) && (k0 + 4 * (f % 4) < ke);
+      const float4 v = in ? r[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      uint2 p0, p1, p2;
+      split3(v, p0, p1, p2);
+      uint16_t* d = s + (f / 4) * PA + 4 * (f % 4);
+      *reinterpret_cast<uint2*>(d) = p0;
+      *reinterpret_cast<uint2*>(d + A_PLANE) = p1;
+      *reinterpret_cast<uint2*>(d + 2 * A_PLANE) = p2;
+    }
+  };
+  // B [K, N], N contiguous: float4 f = tid + 256 q is (k f / 32, n 4 (f % 32))
+  auto load_kmajor = [&](int k0, float4* r) {
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int f = tid + 256 * q;
+      const int k = min(k0 + f / (GT / 4), ke - 1);
+      const int n = min(n0 + 4 * (f % (GT / 4)), g.N - 4);
+      r[q] = *reinterpret_cast<const float4*>(B + static_cast<int64_t>(k) * g.ldb + n);
+    }
+  };
+  auto store_kmajor = [&](uint16_t* s, const float4* r, int k0) {
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int f = tid + 256 * q;
+      const bool in = (k0 + f / (GT / 4) < ke) && (n0 + 4 * (f % (GT / 4)) < g.N);
+      const float4 v = in ? r[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      uint2 p0, p1, p2;
+      split3(v, p0, p1, p2);
+      uint16_t* d = s + (f / (GT / 4)) * PB + 4 * (f % (GT / 4));
+      *reinterpret_cast<uint2*>(d) = p0;
+      *reinterpret_cast<uint2*>(d + B_PLANE) = p1;
+      *reinterpret_cast<uint2*>(d + 2 * B_PLANE) = p2;
+    }
+  };
+  auto load_stage = [&](int st, int slot) {
+    load_rows(A, g.lda, m0, g.M, kb + st * GK, ra[slot]);
+    if constexpr (kTransB) load_rows(B, g.ldb, n0, g.N, kb + st * GK, rb[slot]);
+    else load_kmajor(kb + st * GK, rb[slot]);
+  };
+  auto store_stage = [&](int st, int buf, int slot) {
+    store_rows(sA[buf], ra[slot], m0, g.M, kb + st * GK);
+    if constexpr (kTransB) store_rows(sB[buf], rb[slot], n0, g.N, kb + st * GK);
+    else store_kmajor(sB[buf], rb[slot], kb + st * GK);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  // operand of a 32 x 16 block from a K-contiguous plane: lane l holds row l % 32,
+  // k 8 (l / 32) .. + 7
+  const int l32 = lane & 31, kh = lane >> 5;
+  auto rd_rows = [&](const uint16_t* plane, int r0) -> s16x8v {
+    return *reinterpret_cast<const s16x8v*>(plane + (r0 + l32) * PA + 8 * kh);
+  };
+  // operand of a 16 x 32 block from the N-contiguous plane by two transposing reads
+  // (4 k rows x 4 n-quads per 16 lanes; the second read is 4 k rows further on)
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int tr_n = 16 * (g16 & 1) + 4 * (j16 & 3);
+  const int tr_k = 8 * (g16 >> 1) + (j16 >> 2);
+  auto rd_tr = [&](const uint16_t* plane, int c0) -> s16x8v {
+    const uint16_t* p = plane + tr_k * PB + c0 + tr_n;
+    const s16x4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(p));
+    const s16x4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(p + 4 * PB));
+    return s16x8v{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  };
+
+  // Stages past the K range split to zeros, so the stage count is rounded up to even and
+  // every load and store below is unconditional: with a fixed number of loads in flight
+  // the compiler waits for exactly the stage it stores, never for the one just issued.
+  const int nk = ke > kb ? (ke - kb + GK - 1) / GK : 0;
+  if (nk > 0) {
+    const int nk2 = (nk + 1) & ~1;
+    load_stage(0, 0);
+    load_stage(1, 1);
+    store_stage(0, 0, 0);
+    __syncthreads();
+    // iteration s: loads of stage s + 2 into register slot s % 2 | products of LDS buffer
+    // s % 2 | stage s + 1 (loaded one iteration earlier, slot (s + 1) % 2) into the other
+    // buffer.  Unrolled by two so that the slots are compile-time registers.
+    auto iteration = [&](int s, auto bc) {
+      constexpr int buf = decltype(bc)::value;
+      load_stage(min(s + 2, nk2 - 1), buf);
+      // operand parts are read in the order the products below first need them (a0 b0,
+      // b1, a1, b2, a2), so the first products wait for two reads, not for all twelve
+      s16x8v av[3][2], bv[3][2];
+      auto rd_a = [&](int p) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) av[p][b] = rd_rows(sA[buf] + p * A_PLANE, 64 * wm + 32 * b);
+      };
+      auto rd_b = [&](int p) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          if constexpr (kTransB) bv[p][b] = rd_rows(sB[buf] + p * B_PLANE, 64 * wn + 32 * b);
+          else bv[p][b] = rd_tr(sB[buf] + p * B_PLANE, 64 * wn + 32 * b);
+        }
+      };
+      rd_a(0);
+      rd_b(0);
+      rd_b(1);
+      rd_a(1);
+      rd_b(2);
+      rd_a(2);
+      // parts (i, j) with i + j <= 2; the four blocks interleave so that consecutive
+      // products never wait on one accumulator
+      constexpr int PI[6] = {0, 0, 1, 1, 0, 2};
+      constexpr int PJ[6] = {0, 1, 0, 1, 2, 0};
+#pragma unroll
+      for (int t = 0; t < 6; ++t)
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+          for (int bn = 0; bn < 2; ++bn)
+            acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[PI[t]][bm]),
+                                                                  __builtin_bit_cast(bf16x8, bv[PJ[t]][bn]),
+                                                                  acc[bm][bn], 0, 0, 0);
+      store_stage(s + 1, buf ^ 1, buf ^ 1);   // past the last stage: zeros, never read
+      __syncthreads();
+    };
+    for (int s = 0; s < nk2; s += 2) {
+      iteration(s, std::integral_constant<int, 0>{});
+      iteration(s + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+  // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  const bool has_beta = g.beta != 0.0f;
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) {
+      const int n = n0 + 64 * wn + 32 * bn + l32;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
+        old[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (m < g.M && n < g.N) {
+          const float v = g.alpha * acc[bm][bn][r];
+          C[static_cast<int64_t>(m) * g.ldc + n] = has_beta ? fmaf(g.beta, old[r], v) : v;
+        }
+      }
+    }
+}
+
 }  // namespace
 
 gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
@@ -214,7 +465,14 @@ gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   const bool big = tiles128 >= 512 || (g.flags == 0 && tiles128 >= 256);
   const int T = big ? 128 : 64;
   const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, nz);
-  if (big) {
+  // the split-bf16 kernel loads unmasked 16-byte vectors
+  const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool vec4 = g.K % 4 == 0 && g.N % 4 == 0 && g.lda % 4 == 0 && g.ldb % 4 == 0 && g.sA % 4 == 0 &&
+                    g.sB % 4 == 0 && g.sA2 % 4 == 0 && g.sB2 % 4 == 0 && al16(g.A) && al16(g.B);
+  if (big && vec4) {
+    if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_x6_kernel<false>), grid, dim3(256), 0, stream, g);
+  } else if (big) {
     if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_f32_kernel<false, 128>), grid, dim3(256), 0, stream, g);
   } else {

@@ -8,7 +8,7 @@
 // owns a 256 x 256 tile on or below the diagonal and a slice of the tokens; products of two
 // 16-bit values are exact in fp32 and are summed in fp32 by v_mfma_f32_32x32x16_{bf16,f16}.
 // Token-major X is copied to LDS as it lies in memory by direct global->LDS loads (no
-// register staging; XOR-swizzled 16-byte chunks), with three stages in flight
+// register staging; XOR-swizzled 16-byte chunks), with two stages in flight
 // under the MFMAs; the MFMA operands (8 consecutive tokens of one channel per
 // lane) come out of LDS through the transposing ds_read_b64_tr_b16.
 // Off-diagonal tiles are mirrored into the upper triangle, so H is exactly symmetric.
@@ -30,9 +30,16 @@ namespace {
 
 constexpr int ST = 256;        // output tile edge
 constexpr int SBK = 32;        // tokens per LDS stage
-constexpr int NBUF = 4;        // LDS stage buffers per operand
-constexpr int DEPTH = 3;       // stages in flight ahead of the one being multiplied
-constexpr int SYRK_THREADS = 512;   // 8 waves: 2 (rows) x 4 (columns) of 128 x 64
+// Stages whose copies are in flight ahead of the one being multiplied.  Two beat three
+// and four: the kernel is limited by L2 misses (the 32 concurrent tiles of an XCD stream
+// their 16 channel panels from HBM), and fewer outstanding stages keep more of each
+// panel's lines resident for the other tiles that read it.
+constexpr int DEPTH = 2;
+constexpr int NBUF = DEPTH + 1;          // LDS stage buffers per operand
+// 8 waves per 256 x 256 tile: 2 (rows) x 4 (columns) of 128 x 64, two waves per SIMD.
+// (4 waves of 128 x 128, one per SIMD with the accumulators in AGPRs, read a third fewer
+// operand bytes from LDS but ran slower: one wave per SIMD hides less latency.)
+constexpr int SYRK_WAVES = 8;
 constexpr int kMinTokensPerSplit = 2048;
 
 __device__ __forceinline__ void lower_tile_coords(int t, int& I, int& J) {
@@ -64,11 +71,12 @@ __device__ __forceinline__ void lds_dma16(const void* src, unsigned base) {
       : "memory");
 }
 
-// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their no-wait maxima).
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their no-wait maxima); the
+// counter's low four bits sit in bits 3:0 of the immediate, its high two in bits 15:14.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 
 template <bool kF16>
@@ -86,11 +94,21 @@ __device__ __forceinline__ f32x16 mfma16(s16x4 a0, s16x4 a1, s16x4 b0, s16x4 b1,
 }
 
 // LDS stage layout: SBK token rows of 256 channels (512 bytes), stored as 32 chunks of 16
-// bytes; chunk c of row t sits at physical position c ^ (2 * (t & 3)) so that the four
-// consecutive token rows read together by the transposing loads hit different banks.
-__device__ __forceinline__ int swz_chunk(int t, int c) { return c ^ (2 * (t & 3)); }
+// bytes.  A transposing operand read takes, per 16 lanes, 4 consecutive token rows x 2
+// chunks, and the next 16 lanes the same rows 2 chunks further on; every token row starts
+// on the same bank (512-byte rows, 256 bytes of banks).  Chunk c of row t therefore sits at
+//   phys(t, c) = (c ^ 8 * bit1(c)) ^ 2 * (t & 3):
+// the token term spreads the 4 rows of one 16-lane group over 8 chunks (128 bytes), and
+// the bit-1 term puts the two chunk pairs of a half wave into different 128-byte halves,
+// so the 32 lanes of a half wave cover all 64 banks once.
+__device__ __forceinline__ int chunk_phys(int t, int c) { return (c ^ (((c >> 1) & 1) << 3)) ^ (2 * (t & 3)); }
+// the logical chunk stored at physical position p of row t (inverse of chunk_phys)
+__device__ __forceinline__ int chunk_logical(int t, int p) {
+  const int q = p ^ (2 * (t & 3));
+  return q ^ (((q >> 1) & 1) << 3);
+}
 
-// One 256x256 lower tile and token slice per workgroup of 8 waves (2 x 4 waves of 128 x 64).
+// One 256x256 lower tile and token slice per workgroup of NW waves (2 x NW/2 waves).
 // (tile, slice) pairs are assigned so that each XCD (workgroups are dealt to the 8 XCDs
 // round-robin) works through a contiguous run of tiles of the same slice, which share
 // operand blocks in its L2.
@@ -102,8 +120,8 @@ __device__ __forceinline__ int swz_chunk(int t, int c) { return c ^ (2 * (t & 3)
 //
 // partial == nullptr: H += 2 * tile (and its mirror).  Otherwise the raw tile goes to
 // partial[e][slice][tile][256][256] for syrk_reduce_kernel.
-template <bool kF16>
-__global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
+template <bool kF16, int NW>
+__global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, int d_in,
     int64_t tokens_per_split, int ksplit, float* __restrict__ H, int64_t bsh, float* __restrict__ partial,
     int ntiles) {
@@ -131,24 +149,30 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  constexpr int WN = NW / 2;              // waves along the columns
+  constexpr int WC = ST / WN;              // columns per wave: 64 or 128
+  constexpr int BN = WC / 32;              // 32-column MFMA blocks per wave
+  constexpr int RPW = SBK / NW;            // token rows each wave copies per operand and stage
+  constexpr int CPO = RPW / 2;             // 2-row copies per operand per wave and stage
+  const int wm = wave / WN, wn = wave % WN;
 
-  // Stage loader.  Fast path (all 32 rows and all 256 channels valid): each wave issues 2
+  // Stage loader.  Fast path (all 32 rows and all 256 channels valid): each wave issues CPO
   // direct global->LDS copies of 2 token rows (64 lanes x 16 bytes, lane-linear in LDS)
   // per operand; lane l fills physical chunk l%32 of its row, i.e. fetches logical chunk
-  // (l%32) ^ swizzle.  The per-lane sources of stage 0 and the wave's LDS offsets are
-  // computed once; stage k adds k * SBK rows.  Tail stages go through registers with
-  // zero fill.
-  const int crow = 4 * wave + (lane >> 5);                 // + 2 for the second copy
-  const uint16_t* srcA0 = Xe + (t_begin + crow) * ldx + I0 + 8 * swz_chunk(crow, lane & 31);
-  const uint16_t* srcA1 = Xe + (t_begin + crow + 2) * ldx + I0 + 8 * swz_chunk(crow + 2, lane & 31);
-  const uint16_t* srcB0 = Xe + (t_begin + crow) * ldx + J0 + 8 * swz_chunk(crow, lane & 31);
-  const uint16_t* srcB1 = Xe + (t_begin + crow + 2) * ldx + J0 + 8 * swz_chunk(crow + 2, lane & 31);
+  // chunk_logical(row, l%32).  The per-lane sources of stage 0 and the wave's LDS offsets are
+  // computed once; stage k adds k * SBK rows.  Copy i covers rows crow + 2 i; the swizzle
+  // repeats every 4 rows, so copies i and i + 2 share a source pattern 4 rows apart.
+  // Tail stages go through registers with zero fill.
+  const int crow = RPW * wave + (lane >> 5);
+  const uint16_t* srcA0 = Xe + (t_begin + crow) * ldx + I0 + 8 * chunk_logical(crow, lane & 31);
+  const uint16_t* srcA1 = Xe + (t_begin + crow + 2) * ldx + I0 + 8 * chunk_logical(crow + 2, lane & 31);
+  const uint16_t* srcB0 = Xe + (t_begin + crow) * ldx + J0 + 8 * chunk_logical(crow, lane & 31);
+  const uint16_t* srcB1 = Xe + (t_begin + crow + 2) * ldx + J0 + 8 * chunk_logical(crow + 2, lane & 31);
   constexpr unsigned kBufBytes = SBK * ST * 2, kRowBytes = ST * 2;
   const unsigned ldsA = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(&sA[0][0]))) +
-                        4 * wave * kRowBytes;
+                        RPW * wave * kRowBytes;
   const unsigned ldsB = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(&sB[0][0]))) +
-                        4 * wave * kRowBytes;
+                        RPW * wave * kRowBytes;
   auto load_stage = [&](int k) {
     const int64_t t0 = t_begin + static_cast<int64_t>(k) * SBK;
     const int buf = k % NBUF;
@@ -156,21 +180,29 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
     if (rows == SBK && full_cols) {
       const int64_t off = static_cast<int64_t>(k) * SBK * ldx;
       const unsigned lb = buf * kBufBytes;
-      lds_dma16(srcA0 + off, ldsA + lb);
-      lds_dma16(srcA1 + off, ldsA + lb + 2 * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < CPO; i += 2) {
+        const int64_t o4 = off + static_cast<int64_t>(2 * i) * ldx;   // 4 rows per pair of copies
+        lds_dma16(srcA0 + o4, ldsA + lb + 2 * i * kRowBytes);
+        lds_dma16(srcA1 + o4, ldsA + lb + (2 * i + 2) * kRowBytes);
+      }
       if (!diag) {
-        lds_dma16(srcB0 + off, ldsB + lb);
-        lds_dma16(srcB1 + off, ldsB + lb + 2 * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < CPO; i += 2) {
+          const int64_t o4 = off + static_cast<int64_t>(2 * i) * ldx;
+          lds_dma16(srcB0 + o4, ldsB + lb + 2 * i * kRowBytes);
+          lds_dma16(srcB1 + o4, ldsB + lb + (2 * i + 2) * kRowBytes);
+        }
       }
     } else {
       for (int op = 0; op < (diag ? 1 : 2); ++op) {
         const int C0 = op ? J0 : I0;
         uint16_t* dst = op ? sB[buf] : sA[buf];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 4 * wave + 2 * i + (lane >> 5);
+        for (int i = 0; i < CPO; ++i) {
+          const int r = RPW * wave + 2 * i + (lane >> 5);
           const int p = lane & 31;
-          const int c = swz_chunk(r, p);
+          const int c = chunk_logical(r, p);
           uint4 v = make_uint4(0u, 0u, 0u, 0u);
           if (r < rows && C0 + 8 * c < d_in) v = *reinterpret_cast<const uint4*>(Xe + (t0 + r) * ldx + C0 + 8 * c);
           *reinterpret_cast<uint4*>(dst + r * ST + 8 * p) = v;
@@ -179,11 +211,11 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][BN];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < BN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -197,7 +229,7 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
   auto operand = [&](const uint16_t* stage, int ch0, int tok0) -> s16x4 {
     const int ch = ch0 + op_ch;
     const int t = tok0 + op_tok;
-    const int byte = t * (2 * ST) + 16 * swz_chunk(t, ch >> 3) + 2 * (ch & 7);
+    const int byte = t * (2 * ST) + 16 * chunk_phys(t, ch >> 3) + 2 * (ch & 7);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(reinterpret_cast<const char*>(stage) + byte));
   };
 
@@ -205,18 +237,19 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
   // registers and are complete when issued).  Waiting for a stage means allowing the
   // copies of the `later` stages issued after it to stay outstanding.
   auto wait_copies = [&](int later) {
-    const int n = later * (diag ? 2 : 4);
+    const int n = later * (diag ? CPO : 2 * CPO);
     switch (n) {
       case 0: wait_vmcnt<0>(); break;
       case 2: wait_vmcnt<2>(); break;
       case 4: wait_vmcnt<4>(); break;
       case 6: wait_vmcnt<6>(); break;
-      default: wait_vmcnt<8>(); break;
+      case 8: wait_vmcnt<8>(); break;
+      default: wait_vmcnt<12>(); break;
     }
   };
   // operands of one 16-token half stage
   struct Ops {
-    s16x4 a0[4], a1[4], b0[2], b1[2];
+    s16x4 a0[4], a1[4], b0[BN], b1[BN];
   };
   auto read_ops = [&](int stage, int ks, Ops& o) {
     const uint16_t* as = sA[stage % NBUF];
@@ -227,22 +260,22 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
       o.a1[bm] = operand(as, 128 * wm + 32 * bm, 16 * ks + 4);
     }
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      o.b0[bn] = operand(bs, 64 * wn + 32 * bn, 16 * ks);
-      o.b1[bn] = operand(bs, 64 * wn + 32 * bn, 16 * ks + 4);
+    for (int bn = 0; bn < BN; ++bn) {
+      o.b0[bn] = operand(bs, WC * wn + 32 * bn, 16 * ks);
+      o.b1[bn] = operand(bs, WC * wn + 32 * bn, 16 * ks + 4);
     }
   };
   auto mma = [&](const Ops& o) {
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = mfma16<kF16>(o.a0[bm], o.a1[bm], o.b0[bn], o.b1[bn], acc[bm][bn]);
+      for (int bn = 0; bn < BN; ++bn) acc[bm][bn] = mfma16<kF16>(o.a0[bm], o.a1[bm], o.b0[bn], o.b1[bn], acc[bm][bn]);
     // keep the MFMAs ahead of the following wait/barrier (the compiler would otherwise sink
     // them below it and serialise them with the operand reads)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) asm volatile("" : "+v"(acc[bm][bn]));
+      for (int bn = 0; bn < BN; ++bn) asm volatile("" : "+v"(acc[bm][bn]));
   };
 
   for (int k = 0; k < DEPTH && k < nstages; ++k) load_stage(k);
@@ -274,11 +307,11 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn)
+      for (int bn = 0; bn < BN; ++bn)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = 128 * wm + 32 * bm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int n = 64 * wn + 32 * bn + (lane & 31);
+          const int n = WC * wn + 32 * bn + (lane & 31);
           P[m * ST + n] = acc[bm][bn][r];
         }
     return;
@@ -287,11 +320,11 @@ __global__ __launch_bounds__(SYRK_THREADS) void syrk_mfma_kernel(
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn)
+    for (int bn = 0; bn < BN; ++bn)
 #pragma unroll
       for (int rq4 = 0; rq4 < 4; ++rq4) {
         const int m0 = 128 * wm + 32 * bm + 8 * rq4 + 4 * (lane >> 5);
-        const int n = 64 * wn + 32 * bn + (lane & 31);
+        const int n = WC * wn + 32 * bn + (lane & 31);
         const int col = J0 + n;
         if (col >= d_in) continue;
 #pragma unroll
@@ -561,7 +594,7 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     }
     GPTQ_HIP_TRY(hipEventRecord(ss->join, ss->s));
 
-    const dim3 sblk(SYRK_THREADS);
+    const dim3 sblk(64 * SYRK_WAVES);
     const dim3 grid(pl.ntiles * pl.ksplit, batch);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     float* part = pl.ksplit > 1 ? partial : nullptr;
@@ -569,10 +602,10 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     timing_pair(&ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
-      GPTQ_LAUNCH(syrk_mfma_kernel<true>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit, H,
+      GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit, H,
                   bsh, part, pl.ntiles);
     } else {
-      GPTQ_LAUNCH(syrk_mfma_kernel<false>, grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
+      GPTQ_LAUNCH((syrk_mfma_kernel<false, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
                   H, bsh, part, pl.ntiles);
     }
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
