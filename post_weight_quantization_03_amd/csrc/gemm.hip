@@ -458,17 +458,17 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
 gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0 || g.batch2 <= 0) return GPTQ_OK;
   const int nz = g.batch * g.batch2;
-  // 128-wide tiles when they give every CU two workgroups, or one for a plain product
-  // (triangular operands leave some tiles with far less work, a lower-only output skips
-  // half of them); else 64-wide
+  // 128-wide tiles when they give every CU one workgroup (the split-bf16 kernel, 2.7x the
+  // fp32 rate, even where triangular operands leave some tiles with less work) or, for the
+  // fp32 kernel, two (one for a plain product); else 64-wide fp32 tiles
   const int64_t tiles128 = static_cast<int64_t>((g.N + 127) / 128) * ((g.M + 127) / 128) * nz;
-  const bool big = tiles128 >= 512 || (g.flags == 0 && tiles128 >= 256);
-  const int T = big ? 128 : 64;
-  const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, nz);
   // the split-bf16 kernel loads unmasked 16-byte vectors
   const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec4 = g.K % 4 == 0 && g.N % 4 == 0 && g.lda % 4 == 0 && g.ldb % 4 == 0 && g.sA % 4 == 0 &&
                     g.sB % 4 == 0 && g.sA2 % 4 == 0 && g.sB2 % 4 == 0 && al16(g.A) && al16(g.B);
+  const bool big = vec4 ? tiles128 >= 256 : (tiles128 >= 512 || (g.flags == 0 && tiles128 >= 256));
+  const int T = big ? 128 : 64;
+  const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, nz);
   if (big && vec4) {
     if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_x6_kernel<false>), grid, dim3(256), 0, stream, g);
