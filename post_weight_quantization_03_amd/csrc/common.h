@@ -100,6 +100,7 @@ void timing_pair(hipEvent_t* start, hipEvent_t* stop);
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t join2 = nullptr;   // a second join event, for two side-stream stages in flight
 };
 std::mutex& side_mutex();
 gptq_status side_stream(SideStream** out);   // of the current device

@@ -63,6 +63,7 @@ gptq_status side_stream(SideStream** out) {
     GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
     GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
     GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming));
   }
   *out = &ss;
   return GPTQ_OK;

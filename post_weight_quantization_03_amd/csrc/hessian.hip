@@ -42,6 +42,43 @@ constexpr int NBUF = DEPTH + 1;          // LDS stage buffers per operand
 constexpr int SYRK_WAVES = 8;
 constexpr int kMinTokensPerSplit = 2048;
 
+// (I, J) of lower tile t of an nt x nt tile grid, in an order that keeps concurrent tiles
+// on few channel panels: super-rows of 4 tile rows, within one super-row column chunks of 8
+// tiles, within a chunk row by row.  32 consecutive tiles (one round of an XCD's CUs) then
+// read 4 + 8 = 12 panels; row by row they would read up to 33 on a wide layer.  Scalar
+// loops of at most nt / 4 and nt / 8 iterations.
+__device__ __forceinline__ void blocked_tile_coords(int t, int nt, int& I, int& J) {
+  int r0 = 0;
+  for (;;) {   // super-row
+    const int nr = min(4, nt - r0);
+    // tiles of rows r0 .. r0 + nr - 1: sum of (I + 1)
+    const int cnt = nr * (r0 + 1) + nr * (nr - 1) / 2;
+    if (t < cnt || r0 + nr >= nt) break;
+    t -= cnt;
+    r0 += 4;
+  }
+  const int nr = min(4, nt - r0);
+  for (int c0 = 0;; c0 += 8) {   // column chunk [c0, c0 + 8)
+    int cnt = 0;
+    for (int i = 0; i < nr; ++i) cnt += max(0, min(8, r0 + i + 1 - c0));
+    if (t < cnt || c0 + 8 > r0 + nr - 1) {
+      for (int i = 0; i < nr; ++i) {
+        const int w = max(0, min(8, r0 + i + 1 - c0));
+        if (t < w) {
+          I = r0 + i;
+          J = c0 + t;
+          return;
+        }
+        t -= w;
+      }
+      I = r0;   // not reached for t < nt (nt + 1) / 2
+      J = 0;
+      return;
+    }
+    t -= cnt;
+  }
+}
+
 __device__ __forceinline__ void lower_tile_coords(int t, int& I, int& J) {
   // t enumerates (0,0), (1,0), (1,1), (2,0), ... row by row.
   int i = static_cast<int>((sqrtf(8.0f * static_cast<float>(t) + 1.0f) - 1.0f) * 0.5f);
@@ -118,13 +155,12 @@ __device__ __forceinline__ int chunk_logical(int t, int p) {
 // MFMAs of the current one issue, so neither the copies nor the LDS reads serialise with
 // the matrix cores.
 //
-// partial == nullptr: H += 2 * tile (and its mirror).  Otherwise the raw tile goes to
-// partial[e][slice][tile][256][256] for syrk_reduce_kernel.
+// The raw tile goes to partial[e][slice][tile][256][256]; syrk_reduce_kernel sums the
+// slices in order and adds twice the sum to H and its mirror.
 template <bool kF16, int NW>
 __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, int d_in,
-    int64_t tokens_per_split, int ksplit, float* __restrict__ H, int64_t bsh, float* __restrict__ partial,
-    int ntiles) {
+    int64_t tokens_per_split, int ksplit, float* __restrict__ partial, int ntiles) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][SBK * ST];
   __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][SBK * ST];
 
@@ -139,7 +175,7 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
   const int split = idx / ntiles;
   const int tile = idx - split * ntiles;
   int I, J;
-  lower_tile_coords(tile, I, J);
+  blocked_tile_coords(tile, (d_in + ST - 1) / ST, I, J);
   const bool diag = (I == J);
   const int I0 = I * ST, J0 = J * ST;
   const int64_t t_begin = static_cast<int64_t>(split) * tokens_per_split;
@@ -302,40 +338,16 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
   }
   // Accumulator layout of a 32x32 MFMA block: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  if (partial != nullptr) {
-    float* P = partial + ((static_cast<int64_t>(e) * ksplit + split) * ntiles + tile) * static_cast<int64_t>(ST * ST);
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < BN; ++bn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 128 * wm + 32 * bm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int n = WC * wn + 32 * bn + (lane & 31);
-          P[m * ST + n] = acc[bm][bn][r];
-        }
-    return;
-  }
-  float* He = H + static_cast<int64_t>(e) * bsh;
+  float* Pt = partial + ((static_cast<int64_t>(e) * ksplit + split) * ntiles + tile) * static_cast<int64_t>(ST * ST);
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
     for (int bn = 0; bn < BN; ++bn)
 #pragma unroll
-      for (int rq4 = 0; rq4 < 4; ++rq4) {
-        const int m0 = 128 * wm + 32 * bm + 8 * rq4 + 4 * (lane >> 5);
+      for (int r = 0; r < 16; ++r) {
+        const int m = 128 * wm + 32 * bm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int n = WC * wn + 32 * bn + (lane & 31);
-        const int col = J0 + n;
-        if (col >= d_in) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + q;
-          const int row = I0 + m;
-          if (row >= d_in || (diag && m < n)) continue;
-          const float v = 2.0f * acc[bm][bn][4 * rq4 + q];
-          He[static_cast<int64_t>(row) * d_in + col] += v;
-          if (!diag || m > n) He[static_cast<int64_t>(col) * d_in + row] += v;
-        }
+        Pt[m * ST + n] = acc[bm][bn][r];
       }
 }
 
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   const int sub = blockIdx.x;  // 16 sub-blocks of 64x64
   const int sm = (sub >> 2) * 64, sn = (sub & 3) * 64;
   int I, J;
-  lower_tile_coords(tile, I, J);
+  blocked_tile_coords(tile, (d_in + ST - 1) / ST, I, J);
   const bool diag = (I == J);
   if (diag && sm < sn) return;  // strictly-upper sub-block of a diagonal tile
   const int c4 = 4 * (threadIdx.x & 15), r0 = threadIdx.x >> 4;   // rows r0 + 16 q
@@ -544,7 +556,7 @@ size_t plan_bytes(const HessianPlan& pl, int batch, int d_in, float** partial, d
                   void* ws) {
   Carver cv(ws);
   float* p = nullptr;
-  if (pl.mfma && pl.ksplit > 1)
+  if (pl.mfma)
     p = cv.take<float>(static_cast<size_t>(batch) * pl.ksplit * pl.ntiles * ST * ST);
   double* q = cv.take<double>(static_cast<size_t>(batch) * pl.esplit * d_in);
   if (partial) *partial = p;
@@ -597,22 +609,23 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     const dim3 sblk(64 * SYRK_WAVES);
     const dim3 grid(pl.ntiles * pl.ksplit, batch);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
-    float* part = pl.ksplit > 1 ? partial : nullptr;
+    // Tiles always go through the partial buffer and the ordered reduction, also with a
+    // single token slice: the reduction writes the mirror half through LDS with coalesced
+    // stores, where an epilogue in the SYRK would add to H column by column (one 4-byte
+    // read-modify-write per 128-byte line).
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     timing_pair(&ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
-      GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit, H,
-                  bsh, part, pl.ntiles);
+      GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
+                  partial, pl.ntiles);
     } else {
       GPTQ_LAUNCH((syrk_mfma_kernel<false, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
-                  H, bsh, part, pl.ntiles);
+                  partial, pl.ntiles);
     }
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
-    if (pl.ksplit > 1) {
-      GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
-                  H, bsh);
-    }
+    GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
+                H, bsh);
     GPTQ_HIP_TRY(hipStreamWaitEvent(stream, ss->join, 0));
   } else {
     hipEvent_t ev0 = nullptr, ev1 = nullptr;

@@ -459,17 +459,22 @@ PrepWs carve(void* ws, int batch, int d_in) {
   return w;
 }
 
-// Cholesky of A (lower, in place) into L, blocked by 128 columns, right-looking with a
-// one-block lookahead.  For each block column k, on the main stream:
+// Cholesky of A (lower, in place) into L, blocked by 128 columns, right-looking with
+// lookahead.  For each block column k, on the main stream:
 //   leaf(k):  L_kk and X_kk = L_kk^-1 from the updated diagonal block (potrf_block_kernel);
 //   panel(k): L[k+1:, k] = A[k+1:, k] X_kk^T;
-//   near(k):  A[k+1:, k+1] -= L[k+1:, k] L[k+1, k]^T  (the next block column, so that
-//             leaf(k+1) and panel(k+1) can start);
-// and on the side stream, overlapping leaf(k+1) and panel(k+1):
-//   far(k):   A[k+2:, k+2:] -= L[k+2:, k] L[k+2:, k]^T  (lower tiles).
-// far(k) starts once panel(k) is done; near(k+1) writes block column k+2, which far(k)
-// also writes, so it waits for far(k).  Every block receives the updates of all earlier
-// panels before it is factored: the last one from near, the others from far.
+//   near(k):  A[k+1:, k+1] -= L[k+1:, F:k+1] L[k+1, F:k+1]^T, the panels F..k that no far
+//             update has brought to block column k+1, so that leaf(k+1) and panel(k+1) can start;
+// and on the side stream, every G panels (k + 1 - f == G, f = first panel not yet given to a
+// far update):
+//   far(k):   A[k+3:, k+3:] -= L[k+3:, f:k+1] L[k+3:, f:k+1]^T  (lower tiles, K = 128 G).
+// A far update covers the columns from k+3 on, so near(k+1), which writes column k+2, does
+// not wait for the far update of panel k: the side stream runs up to two steps behind the
+// chain.  near(c-1) waits for the last far update that covers column c (the one launched at
+// a checkpoint <= c-3).  Aggregating G panels per far update reads and rewrites the trailing
+// matrix once per G panels (with K = 128 these updates are bound by that traffic); the near
+// updates then carry K = 2..G+1 panels.  Every block receives the updates of all earlier
+// panels exactly once before it is factored.
 // From this many problems per call on, the Cholesky runs left-looking on one stream.
 constexpr int kLeftLookingBatch = 4;
 
@@ -519,10 +524,23 @@ gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, in
   return GPTQ_OK;
 }
 
+// Panels per far update: one trailing pass per 128 columns while the chain of small
+// products is the critical path (d_in <= 4096: 1, 2 and 4 measured the same); four for wide
+// layers, where the trailing passes bound the factorization (d_in 14336: 26.9 ms with one
+// pass per panel, 22.5 with 2, 21.4 with 4, 22.0 with 8).
+int far_group(int nb) { return nb <= 32 ? 1 : 4; }
+
 gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc) {
   const int nb = sc.nb, batch = sc.batch;
+  const int G = far_group(nb);
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
   hipStream_t s0 = sc.main, s1 = sc.side->s;
+  hipEvent_t far_done[2] = {sc.side->join, sc.side->join2};   // far update i records far_done[i % 2]
+  // checkpoints of the last two far updates (their checkpoints differ by G >= 1, so when
+  // the last one is too recent to cover a column, the one before it does)
+  int last_k[2] = {-1, -1};   // [0]: the one before the last, [1]: the last
+  int nfar = 0;
+  int f = 0;   // first panel not yet given to a far update
   for (int k = 0; k < nb; ++k) {
     GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
     const int rest = nb - k - 1;   // block rows below the diagonal block k
@@ -536,29 +554,46 @@ gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv,
     g.C = block_at(L, d_in, k + 1, k); g.ldc = d_in; g.sC = bsl;
     g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower;
     if ((st = gemm_f32(g, s0)) != GPTQ_OK) return st;
-    GPTQ_HIP_TRY(hipEventRecord(sc.side->fork, s0));           // panel(k) done
-    if (k > 0) GPTQ_HIP_TRY(hipStreamWaitEvent(s0, sc.side->join, 0));   // far(k-1) done
+    // near(k) writes column c = k + 1: the last far update covering it has checkpoint <= k - 2
+    int F = 0, wait = -1;
+    if (nfar >= 1 && last_k[1] <= k - 2) {
+      F = last_k[1] + 1;
+      wait = nfar - 1;
+    } else if (nfar >= 2 && last_k[0] <= k - 2) {
+      F = last_k[0] + 1;
+      wait = nfar - 2;
+    }
+    // a far update at checkpoint k: panels f..k onto the columns from k + 3 on
+    const bool far_now = (k + 1 - f == G) && (k + 3 <= nb - 1);
+    if (far_now) GPTQ_HIP_TRY(hipEventRecord(sc.side->fork, s0));   // panel(k) done
+    if (wait >= 0) GPTQ_HIP_TRY(hipStreamWaitEvent(s0, far_done[wait & 1], 0));
     GemmArgs n{};
     n.batch = batch;
-    n.M = rest * NB; n.N = NB; n.K = NB;
-    n.A = block_at(L, d_in, k + 1, k); n.lda = d_in; n.sA = bsl;
-    n.B = n.A; n.ldb = d_in; n.sB = bsl;                         // rows of L[k+1, k]
+    n.M = rest * NB; n.N = NB; n.K = (k + 1 - F) * NB;
+    n.A = block_at(L, d_in, k + 1, F); n.lda = d_in; n.sA = bsl;
+    n.B = n.A; n.ldb = d_in; n.sB = bsl;                         // block row k+1 of L
     n.C = block_at(A, d_in, k + 1, k + 1); n.ldc = d_in; n.sC = dd;
     n.alpha = -1.0f; n.beta = 1.0f; n.transB = 1; n.flags = 0;
     if ((st = gemm_f32(n, s0)) != GPTQ_OK) return st;
-    if (rest >= 2) {
+    if (far_now) {
       GPTQ_HIP_TRY(hipStreamWaitEvent(s1, sc.side->fork, 0));
-      GemmArgs f{};
-      f.batch = batch;
-      f.M = (rest - 1) * NB; f.N = (rest - 1) * NB; f.K = NB;
-      f.A = block_at(L, d_in, k + 2, k); f.lda = d_in; f.sA = bsl;
-      f.B = f.A; f.ldb = d_in; f.sB = bsl;
-      f.C = block_at(A, d_in, k + 2, k + 2); f.ldc = d_in; f.sC = dd;
-      f.alpha = -1.0f; f.beta = 1.0f; f.transB = 1; f.flags = kLowerOut;
-      if ((st = gemm_f32(f, s1)) != GPTQ_OK) return st;
-      GPTQ_HIP_TRY(hipEventRecord(sc.side->join, s1));
+      GemmArgs u{};
+      u.batch = batch;
+      u.M = (nb - k - 3) * NB; u.N = u.M; u.K = (k + 1 - f) * NB;
+      u.A = block_at(L, d_in, k + 3, f); u.lda = d_in; u.sA = bsl;
+      u.B = u.A; u.ldb = d_in; u.sB = bsl;
+      u.C = block_at(A, d_in, k + 3, k + 3); u.ldc = d_in; u.sC = dd;
+      u.alpha = -1.0f; u.beta = 1.0f; u.transB = 1; u.flags = kLowerOut;
+      if ((st = gemm_f32(u, s1)) != GPTQ_OK) return st;
+      GPTQ_HIP_TRY(hipEventRecord(far_done[nfar & 1], s1));
+      last_k[0] = last_k[1];
+      last_k[1] = k;
+      ++nfar;
+      f = k + 1;
     }
   }
+  // every far update has been joined by a later near update; join the last one anyway
+  if (nfar > 0) GPTQ_HIP_TRY(hipStreamWaitEvent(s0, far_done[(nfar - 1) & 1], 0));
   return GPTQ_OK;
 }
 
