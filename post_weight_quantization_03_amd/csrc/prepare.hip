@@ -177,8 +177,11 @@ __global__ __launch_bounds__(256) void gather_reversed_scalar_kernel(const float
 // (X = L^-1).  A 16-column leaf is factored and inverted by one wave with the 16 rows in
 // lanes 0..15 and the columns in registers; values move between lanes by readlane, so a
 // leaf needs no barrier.  Products are 16x16 output tiles on the fp32 matrix cores,
-// dealt round-robin to the four waves, with one barrier per product.
+// dealt round-robin to the LEAF_WAVES waves, with one barrier per product.
 constexpr int LLD = NB + 4;   // LDS row stride (floats): 16-byte aligned rows, banks spread
+// Waves of the diagonal-block kernel: the 16x16 tile products of a level are dealt to them
+// (at the top level 26 tiles: 2 rounds with 16 waves, 7 with 4).
+constexpr int LEAF_WAVES = 16;
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -301,7 +304,7 @@ __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave,
     if (wave == 0) leaf16<kFirst>(sA, sX, o, lane, bad);
     __syncthreads();
   } else {
-    constexpr int H = S / 2, NT = H / 16, NTT = NT * NT, PER = (NTT + 3) / 4;
+    constexpr int H = S / 2, NT = H / 16, NTT = NT * NT, PER = (NTT + LEAF_WAVES - 1) / LEAF_WAVES;
     leaf_node<H, true>(sA, sX, o, wave, lane, bad);
     const f32x4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4v res[PER];
@@ -309,7 +312,7 @@ __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave,
       // L21 = A21 X11^T (X11 lower: k < 16 (tj + 1)), in place over A21
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int t = wave + 4 * u;
+        const int t = wave + LEAF_WAVES * u;
         if (t < NTT) {
           const int ti = t / NT, tj = t % NT;
           res[u] = tile_mma<true>(zero, sA + (o + H + 16 * ti) * LLD + o, sX + (o + 16 * tj) * LLD + o, 0,
@@ -319,14 +322,14 @@ __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave,
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int t = wave + 4 * u;
+        const int t = wave + LEAF_WAVES * u;
         if (t < NTT) tile_store(sA + (o + H + 16 * (t / NT)) * LLD + o + 16 * (t % NT), res[u], lane);
       }
       __syncthreads();
     }
     // S22 = A22 - L21 L21^T (lower tiles) and T = L21 X11 (X11 lower: k >= 16 tj) into X21
     constexpr int NLOW = NT * (NT + 1) / 2;
-    for (int t = wave; t < NLOW + NTT; t += 4) {
+    for (int t = wave; t < NLOW + NTT; t += LEAF_WAVES) {
       if (t < NLOW) {
         int ti = 0;
         while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
@@ -347,7 +350,7 @@ __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave,
     // X21 = -X22 T (X22 lower: k < 16 (ti + 1)), in place over T
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + LEAF_WAVES * u;
       if (t < NTT) {
         const int ti = t / NT, tj = t % NT;
         res[u] = tile_mma<false>(zero, sX + (o + H + 16 * ti) * LLD + o + H, sX + (o + H) * LLD + o + 16 * tj, 0,
@@ -357,14 +360,14 @@ __device__ __forceinline__ void leaf_node(float* sA, float* sX, int o, int wave,
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + LEAF_WAVES * u;
       if (t < NTT) tile_store(sX + (o + H + 16 * (t / NT)) * LLD + o + 16 * (t % NT), -res[u], lane);
     }
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(256) void potrf_block_kernel(const float* __restrict__ A, float* __restrict__ Lbuf,
+__global__ __launch_bounds__(64 * LEAF_WAVES) void potrf_block_kernel(const float* __restrict__ A, float* __restrict__ Lbuf,
                                                           int64_t bsl, float* __restrict__ Linv, int d_in,
                                                           int k0, int* __restrict__ flag) {
   __shared__ __attribute__((aligned(16))) float sA[NB * LLD];
@@ -375,21 +378,23 @@ __global__ __launch_bounds__(256) void potrf_block_kernel(const float* __restric
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
   const float* Ae = A + e * dd + static_cast<int64_t>(k0) * d_in + k0;
   if (t == 0) bad = 0;
-  // 128 rows x 32 float4: thread t loads float4 column t%32 of rows t/32 + 8 m
-#pragma unroll 4
-  for (int m = 0; m < NB / 8; ++m) {
-    const int row = t / 32 + 8 * m, c4 = t % 32;
-    *reinterpret_cast<float4*>(sA + row * LLD + 4 * c4) =
-        *reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(row) * d_in + 4 * c4);
-  }
+  // 128 rows x 32 float4: thread t loads float4 column t%32 of rows t/32 + RS m, all loads
+  // issued before the first LDS store
+  constexpr int RS = 2 * LEAF_WAVES, NM = NB / RS;
+  float4 ld[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+    ld[m] = *reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(t / 32 + RS * m) * d_in + 4 * (t % 32));
+#pragma unroll
+  for (int m = 0; m < NM; ++m) *reinterpret_cast<float4*>(sA + (t / 32 + RS * m) * LLD + 4 * (t % 32)) = ld[m];
   __syncthreads();
   leaf_node<NB, false>(sA, sX, 0, wave, lane, &bad);
   if (t == 0 && bad) flag[e] = 1;
   float* Le = Lbuf + e * bsl + static_cast<int64_t>(k0) * d_in + k0;
   float* Xe = Linv + e * dd + static_cast<int64_t>(k0) * d_in + k0;
-#pragma unroll 4
-  for (int m = 0; m < NB / 8; ++m) {
-    const int row = t / 32 + 8 * m, c = 4 * (t % 32);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int row = t / 32 + RS * m, c = 4 * (t % 32);
     const float4 l = *reinterpret_cast<const float4*>(sA + row * LLD + c);
     const float4 x = *reinterpret_cast<const float4*>(sX + row * LLD + c);
     *reinterpret_cast<float4*>(Le + static_cast<int64_t>(row) * d_in + c) =
@@ -509,7 +514,7 @@ gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, in
       u.alpha = -1.0f; u.beta = 1.0f; u.transB = 1; u.flags = 0;
       if ((st = gemm_f32(u, s0)) != GPTQ_OK) return st;
     }
-    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
+    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(64 * LEAF_WAVES), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
     const int rest = nb - k - 1;
     if (rest == 0) break;
     GemmArgs g{};
@@ -542,7 +547,7 @@ gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv,
   int nfar = 0;
   int f = 0;   // first panel not yet given to a far update
   for (int k = 0; k < nb; ++k) {
-    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(256), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
+    GPTQ_LAUNCH(potrf_block_kernel, dim3(batch), dim3(64 * LEAF_WAVES), 0, s0, A, L, bsl, Linv, d_in, k * NB, flag);
     const int rest = nb - k - 1;   // block rows below the diagonal block k
     if (rest == 0) break;
     gptq_status st;
