@@ -529,11 +529,13 @@ gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, in
   return GPTQ_OK;
 }
 
-// Panels per far update: one trailing pass per 128 columns while the chain of small
-// products is the critical path (d_in <= 4096: 1, 2 and 4 measured the same); four for wide
-// layers, where the trailing passes bound the factorization (d_in 14336: 26.9 ms with one
-// pass per panel, 22.5 with 2, 21.4 with 4, 22.0 with 8).
-int far_group(int nb) { return nb <= 32 ? 1 : 4; }
+// Panels per far update.  While the chain of small products is the critical path (d_in <=
+// 4096) two: every fork/join between the streams adds a few microseconds to the chain, and
+// near updates of up to three panels are still short (attn_proj prepare 2.73 ms with one,
+// 2.63 with two, 2.66 with three).  Four for wide layers, where the trailing passes bound
+// the factorization (d_in 14336: 26.9 ms with one pass per panel, 22.5 with 2, 21.4 with
+// 4, 22.0 with 8).
+int far_group(int nb) { return nb <= 32 ? 2 : 4; }
 
 gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc) {
   const int nb = sc.nb, batch = sc.batch;
