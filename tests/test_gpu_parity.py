@@ -47,6 +47,10 @@ CASES = {
     "per_row_4_lanes": synth.scaled("moe", d_out=520, d_in=256, n_tokens=600, batch=24, seq_len=300,
                                     group_size=-1),
     "group128_4_lanes_512": synth.scaled("moe", d_out=512, d_in=128, n_tokens=400, batch=64, seq_len=200),
+    # 36 block columns: the Cholesky's far updates grouped four panels at a time; lazy updates,
+    # trailing updates and the triangular inverse large enough for the split-bf16 products
+    # (ragged row tiles: 1944 = 15 x 128 + 24; both B layouts; lower-only output)
+    "wide_dense_grouped": synth.scaled("mlp_down", d_out=1944, d_in=4608, n_tokens=6000, seq_len=1000),
 }
 
 
