@@ -221,16 +221,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 // Six v_mfma_f32_32x32x16_bf16 per 32x32x16 block run at 2500 / 6 = 417 TFLOP/s of fp32
 // products against 157 TFLOP/s for v_mfma_f32_32x32x2_f32.
 //
-// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 blocks of 32 x 32), two
-// workgroups per CU.  The three parts are stored in LDS as bf16 planes: A (and B^T) with K
-// contiguous per row, read as 16 bytes per lane (rows 48 bytes apart: a 16-lane read
-// covers all banks once); B [K, N] with N contiguous, read with the transposing
-// ds_read_b64_tr_b16 (k rows 320 bytes apart: a half wave covers all banks once).
+// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 blocks of 32 x 32), two or
+// three workgroups per CU.  The three parts are stored in LDS as bf16 planes: A (and B^T)
+// with K contiguous per row, 32 bytes = two 16-byte chunks per row, the chunks of rows
+// 8..15 (mod 16) swapped, so that a 16-lane read of 16 bytes per lane (rows r..r+15, one k
+// half) and a 32-lane write of 8 bytes per lane (8 whole rows) each cover all 64 banks
+// once; B [K, N] with N contiguous, read with the transposing ds_read_b64_tr_b16 (k rows
+// 320 bytes apart: a half wave covers all banks once).
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 typedef short s16x8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4v lds_s16x4v;
+
+// 16-byte chunk swap of K-contiguous plane rows 8..15 (mod 16)
+__device__ __forceinline__ int chunk_swz(int row) { return (row >> 3) & 1; }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2v v = {a, b};
@@ -253,7 +258,7 @@ __device__ __forceinline__ void split3(const float4 v, uint2& p0, uint2& p1, uin
 template <bool kTransB>
 __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   constexpr int GT = 128, GK = 16;
-  constexpr int PA = GK + 8;                   // bf16 per K-contiguous row
+  constexpr int PA = GK;                       // bf16 per K-contiguous row (two 16-byte chunks)
   constexpr int PB = GT + 32;                  // bf16 per k row of the N-contiguous layout
   constexpr int A_PLANE = GT * PA;
   constexpr int B_PLANE = kTransB ? GT * PA : GK * PB;
@@ -304,7 +309,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
       const float4 v = in ? r[q] : make_float4(0.f, 0.f, 0.f, 0.f);
       uint2 p0, p1, p2;
       split3(v, p0, p1, p2);
-      uint16_t* d = s + (f / 4) * PA + 4 * (f % 4);
+      const int row = f / 4, k4 = f % 4;
+      uint16_t* d = s + row * PA + 8 * ((k4 >> 1) ^ chunk_swz(row)) + 4 * (k4 & 1);
       *reinterpret_cast<uint2*>(d) = p0;
       *reinterpret_cast<uint2*>(d + A_PLANE) = p1;
       *reinterpret_cast<uint2*>(d + 2 * A_PLANE) = p2;
@@ -357,7 +363,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   // k 8 (l / 32) .. + 7
   const int l32 = lane & 31, kh = lane >> 5;
   auto rd_rows = [&](const uint16_t* plane, int r0) -> s16x8v {
-    return *reinterpret_cast<const s16x8v*>(plane + (r0 + l32) * PA + 8 * kh);
+    const int row = r0 + l32;
+    return *reinterpret_cast<const s16x8v*>(plane + row * PA + 8 * (kh ^ chunk_swz(row)));
   };
   // operand of a 16 x 32 block from the N-contiguous plane by two transposing reads
   // (4 k rows x 4 n-quads per 16 lanes; the second read is 4 k rows further on)
