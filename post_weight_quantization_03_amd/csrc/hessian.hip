@@ -8,7 +8,7 @@
 // owns a 256 x 256 tile on or below the diagonal and a slice of the tokens; products of two
 // 16-bit values are exact in fp32 and are summed in fp32 by v_mfma_f32_32x32x16_{bf16,f16}.
 // Token-major X is copied to LDS as it lies in memory by direct global->LDS loads (no
-// register staging; XOR-swizzled 16-byte chunks), with two stages in flight
+// register staging; XOR-swizzled 16-byte chunks), one 64-token stage in flight
 // under the MFMAs; the MFMA operands (8 consecutive tokens of one channel per
 // lane) come out of LDS through the transposing ds_read_b64_tr_b16.
 // Off-diagonal tiles are mirrored into the upper triangle, so H is exactly symmetric.
@@ -29,13 +29,16 @@ namespace gptq {
 namespace {
 
 constexpr int ST = 256;        // output tile edge
-constexpr int SBK = 32;        // tokens per LDS stage
-// Stages whose copies are in flight ahead of the one being multiplied.  Two beat three
-// and four: the kernel is limited by L2 misses (the 32 concurrent tiles of an XCD stream
-// their 16 channel panels from HBM), and fewer outstanding stages keep more of each
-// panel's lines resident for the other tiles that read it.
-constexpr int DEPTH = 2;
-constexpr int NBUF = DEPTH + 1;          // LDS stage buffers per operand
+constexpr int SBK = 64;        // tokens per LDS stage
+// Two stage buffers per operand: while stage s is multiplied, the copy of stage s + 1 is in
+// flight.  Each wave drains its own LDS reads of stage s (lgkmcnt(0)) before the stage's one
+// barrier, after which the copy of stage s + 2 goes into stage s's buffer.  64-token stages
+// (four 16-token MFMA steps per barrier) ran 7-10% faster than 32-token stages with three
+// buffers and the same bytes in flight; with 32-token stages, two stages in flight beat
+// three and four (fewer outstanding copies keep more of each channel panel's lines in L2
+// for the other tiles of the round that read it).
+constexpr int DEPTH = 2;                  // stages loaded before the first barrier
+constexpr int NBUF = 2;                   // LDS stage buffers per operand
 // 8 waves per 256 x 256 tile: 2 (rows) x 4 (columns) of 128 x 64, two waves per SIMD.
 // (4 waves of 128 x 128, one per SIMD with the accumulators in AGPRs, read a third fewer
 // operand bytes from LDS but ran slower: one wave per SIMD hides less latency.)
@@ -150,8 +153,8 @@ __device__ __forceinline__ int chunk_logical(int t, int p) {
 // round-robin) works through a contiguous run of tiles of the same slice, which share
 // operand blocks in its L2.
 //
-// Global->LDS copies run DEPTH stages ahead of the math, and within the math the operand
-// reads (transposing LDS reads) of the next 16-token half stage are in flight while the
+// Global->LDS copies run one stage ahead of the math, and within the math the operand
+// reads (transposing LDS reads) of the next 16-token step are in flight while the
 // MFMAs of the current one issue, so neither the copies nor the LDS reads serialise with
 // the matrix cores.
 //
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
       default: wait_vmcnt<12>(); break;
     }
   };
-  // operands of one 16-token half stage
+  // operands of one 16-token step
   struct Ops {
     s16x4 a0[4], a1[4], b0[BN], b1[BN];
   };
@@ -315,24 +318,29 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
   };
 
   for (int k = 0; k < DEPTH && k < nstages; ++k) load_stage(k);
-  Ops P, Q;   // half-stage operand sets: P = (stage, first half), Q = (stage, second half)
+  Ops P, Q;   // operand sets of alternate 16-token steps
   if (nstages > 0) {
     wait_copies(min(DEPTH, nstages) - 1);
     __syncthreads();
     read_ops(0, 0, P);
   }
-  // Each stage runs in two phases; in each, the MFMAs of one half stage are issued while
-  // the operand reads of the next half stage are in flight:
-  //   phase 1: read (s, second half) | MFMAs (s, first half) ; wait for stage s+1, barrier;
-  //            start the copy of stage s+DEPTH into the buffer of stage s-1 (every wave is
-  //            past the barrier, so done with stage s-1)
-  //   phase 2: read (s+1, first half) | MFMAs (s, second half)
+  // Each stage runs in four 16-token steps; in each, the MFMAs of one step are issued while
+  // the operand reads of the next step are in flight (P and Q alternate):
+  //   read (s, 1) | MFMAs (s, 0);  read (s, 2) | MFMAs (s, 1);  read (s, 3) | MFMAs (s, 2);
+  //   wait for the copies of stage s+1 and for this wave's reads of stage s, barrier;
+  //   start the copy of stage s+2 into stage s's buffer;
+  //   read (s+1, 0) | MFMAs (s, 3)
   for (int s = 0; s < nstages; ++s) {
     read_ops(s, 1, Q);
     mma(P);
-    if (s + 1 < nstages) wait_copies(min(s + DEPTH - 1, nstages - 1) - (s + 1));
+    read_ops(s, 2, P);
+    mma(Q);
+    read_ops(s, 3, Q);
+    mma(P);
+    if (s + 1 < nstages) wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of stage s are done
     __syncthreads();
-    if (s + DEPTH < nstages) load_stage(s + DEPTH);
+    if (s + 2 < nstages) load_stage(s + 2);   // into the buffer of stage s
     if (s + 1 < nstages) read_ops(s + 1, 0, P);
     mma(Q);
   }
