@@ -226,8 +226,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 // with K contiguous per row, 32 bytes = two 16-byte chunks per row, the chunks of rows
 // 8..15 (mod 16) swapped, so that a 16-lane read of 16 bytes per lane (rows r..r+15, one k
 // half) and a 32-lane write of 8 bytes per lane (8 whole rows) each cover all 64 banks
-// once; B [K, N] with N contiguous, read with the transposing ds_read_b64_tr_b16 (k rows
-// 320 bytes apart: a half wave covers all banks once).
+// once; B [K, N] with N contiguous, 256-byte k rows with the 8-byte n-quads of rows k+1..3
+// (mod 4) moved by 64 bytes each, read with the transposing ds_read_b64_tr_b16 (a half wave
+// covers all banks once).  48 KB of LDS per workgroup either way: three fit a CU.
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short s16x4v __attribute__((ext_vector_type(4)));
@@ -236,6 +237,10 @@ typedef __attribute__((address_space(3))) s16x4v lds_s16x4v;
 
 // 16-byte chunk swap of K-contiguous plane rows 8..15 (mod 16)
 __device__ __forceinline__ int chunk_swz(int row) { return (row >> 3) & 1; }
+// physical 8-byte n-quad of quad q in k row k of an N-contiguous plane (256-byte rows): rows
+// k, k+1, k+2, k+3 move their quads by 64 bytes each, so the 4 rows x 8 quads of a half
+// wave's transposing read, and a 32-lane write of one row, cover all 64 banks once
+__device__ __forceinline__ int quad_swz(int k, int q) { return q ^ (8 * (k & 3)); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2v v = {a, b};
@@ -259,7 +264,7 @@ template <bool kTransB>
 __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   constexpr int GT = 128, GK = 16;
   constexpr int PA = GK;                       // bf16 per K-contiguous row (two 16-byte chunks)
-  constexpr int PB = GT + 32;                  // bf16 per k row of the N-contiguous layout
+  constexpr int PB = GT;                       // bf16 per k row of the N-contiguous layout
   constexpr int A_PLANE = GT * PA;
   constexpr int B_PLANE = kTransB ? GT * PA : GK * PB;
   constexpr int RQ = GT * GK / 1024;           // float4 per thread per operand and stage (2)
@@ -334,7 +339,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
       const float4 v = in ? r[q] : make_float4(0.f, 0.f, 0.f, 0.f);
       uint2 p0, p1, p2;
       split3(v, p0, p1, p2);
-      uint16_t* d = s + (f / (GT / 4)) * PB + 4 * (f % (GT / 4));
+      const int k = f / (GT / 4);
+      uint16_t* d = s + k * PB + 4 * quad_swz(k, f % (GT / 4));
       *reinterpret_cast<uint2*>(d) = p0;
       *reinterpret_cast<uint2*>(d + B_PLANE) = p1;
       *reinterpret_cast<uint2*>(d + 2 * B_PLANE) = p2;
@@ -372,7 +378,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   const int tr_n = 16 * (g16 & 1) + 4 * (j16 & 3);
   const int tr_k = 8 * (g16 >> 1) + (j16 >> 2);
   auto rd_tr = [&](const uint16_t* plane, int c0) -> s16x8v {
-    const uint16_t* p = plane + tr_k * PB + c0 + tr_n;
+    const int q = (c0 + tr_n) >> 2;   // the lane's n-quad; rows tr_k and tr_k + 4 share k mod 4
+    const uint16_t* p = plane + tr_k * PB + 4 * quad_swz(tr_k, q);
     const s16x4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(p));
     const s16x4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(p + 4 * PB));
     return s16x8v{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
