@@ -28,7 +28,12 @@ namespace {
 // TT = output tile edge (128 or 64); each of the 4 waves owns a (TT/2) x (TT/2) quarter as
 // MB x MB blocks of 32 x 32.  The 64-wide tile takes 64 k per stage: with one workgroup per
 // CU its stage is otherwise too short to cover the latency of the next stage's loads.
-template <bool kTransB, int TT>
+// kVec: K, N and the leading dimensions are multiples of 4 and the operands 16-byte aligned;
+// loads are then unconditional 16-byte loads from clamped addresses, with the elements
+// outside the product zeroed when the stage is stored to LDS.  (Editing a loaded register
+// right after its load, as the general path does for a partial vector, makes the compiler
+// wait for every load as it is issued.)
+template <bool kTransB, int TT, bool kVec>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int GT = TT;
   constexpr int GK = TT == 64 ? 64 : 32;
@@ -74,6 +79,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     for (int q = 0; q < RQ; ++q) {
       const int row = r0 + lr + RS * q;
       const int k = k0 + 4 * lc;
+      if constexpr (kVec) {
+        r[q] = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(min(row, rlim - 1)) * ld + min(k, ke - 4));
+        continue;
+      }
       if (row < rlim && k < ke) {
         r[q] = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(row) * ld + k);
         if (k + 4 > ke) {  // partial K vector: zero the tail
@@ -86,15 +95,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
     }
   };
-  auto store_rows = [&](auto s, const float4* r) {
+  auto store_rows = [&](auto s, const float4* r, int r0, int rlim, int k0) {
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
       const int row = lr + RS * q;
       const int k = 4 * lc;
-      s[k + 0][row] = r[q].x;
-      s[k + 1][row] = r[q].y;
-      s[k + 2][row] = r[q].z;
-      s[k + 3][row] = r[q].w;
+      float4 v = r[q];
+      if constexpr (kVec) {
+        if (!(r0 + row < rlim && k0 + k < ke)) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      s[k + 0][row] = v.x;
+      s[k + 1][row] = v.y;
+      s[k + 2][row] = v.z;
+      s[k + 3][row] = v.w;
     }
   };
   // B tile [GK k][GT n] (no transpose): thread loads k = tid / (GT/4) + (256*4/GT) q,
@@ -106,6 +119,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     for (int q = 0; q < RQ; ++q) {
       const int k = k0 + tid / NV + KS * q;
       const int n = n0 + 4 * (tid % NV);
+      if constexpr (kVec) {
+        r[q] = *reinterpret_cast<const float4*>(B + static_cast<int64_t>(min(k, ke - 1)) * g.ldb + min(n, g.N - 4));
+        continue;
+      }
       if (k < ke && n < g.N) {
         if (n + 4 <= g.N) {
           r[q] = *reinterpret_cast<const float4*>(B + static_cast<int64_t>(k) * g.ldb + n);
@@ -121,20 +138,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
     }
   };
-  auto store_kmajor = [&](float (*s)[GPB], const float4* r) {
+  auto store_kmajor = [&](float (*s)[GPB], const float4* r, int k0) {
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
       const int k = tid / NV + KS * q;
-      *reinterpret_cast<float4*>(&s[k][4 * (tid % NV)]) = r[q];
+      float4 v = r[q];
+      if constexpr (kVec) {
+        if (!(k0 + k < ke && n0 + 4 * (tid % NV) < g.N)) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      *reinterpret_cast<float4*>(&s[k][4 * (tid % NV)]) = v;
     }
   };
   auto load_b = [&](int k0) {
     if constexpr (kTransB) load_rows(B, g.ldb, n0, g.N, k0, rb);
     else load_kmajor(k0, rb);
   };
-  auto store_b = [&](float (*s)[GPB]) {
-    if constexpr (kTransB) store_rows(s, rb);
-    else store_kmajor(s, rb);
+  auto store_b = [&](float (*s)[GPB], int k0) {
+    if constexpr (kTransB) store_rows(s, rb, n0, g.N, k0);
+    else store_kmajor(s, rb, k0);
   };
 
   f32x16 acc[MB][MB];
@@ -149,8 +170,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if (nk > 0) {
     load_rows(A, g.lda, m0, g.M, kb, ra);
     load_b(kb);
-    store_rows(sA[0], ra);
-    store_b(sB[0]);
+    store_rows(sA[0], ra, m0, g.M, kb);
+    store_b(sB[0], kb);
   }
   __syncthreads();
   const int l32 = lane & 31, kh = lane >> 5;
@@ -176,8 +197,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
           acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[bm], bv[bn], acc[bm][bn], 0, 0, 0);
     }
     if (more) {
-      store_rows(sA[buf ^ 1], ra);
-      store_b(sB[buf ^ 1]);
+      store_rows(sA[buf ^ 1], ra, m0, g.M, kb + (s + 1) * GK);
+      store_b(sB[buf ^ 1], kb + (s + 1) * GK);
     }
     __syncthreads();
   }
@@ -487,11 +508,14 @@ gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
     if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_x6_kernel<false>), grid, dim3(256), 0, stream, g);
   } else if (big) {
-    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128>), grid, dim3(256), 0, stream, g);
-    else GPTQ_LAUNCH((gemm_f32_kernel<false, 128>), grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128, false>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 128, false>), grid, dim3(256), 0, stream, g);
+  } else if (vec4) {
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64, true>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, true>), grid, dim3(256), 0, stream, g);
   } else {
-    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64>), grid, dim3(256), 0, stream, g);
-    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64>), grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64, false>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false>), grid, dim3(256), 0, stream, g);
   }
   return GPTQ_OK;
 }
