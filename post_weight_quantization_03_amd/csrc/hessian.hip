@@ -11,16 +11,15 @@
 // register staging; XOR-swizzled 16-byte chunks), one 64-token stage in flight
 // under the MFMAs; the MFMA operands (8 consecutive tokens of one channel per
 // lane) come out of LDS through the transposing ds_read_b64_tr_b16.
-// Off-diagonal tiles are mirrored into the upper triangle, so H is exactly symmetric.
-// When the tiles alone cannot fill the 256 CUs the tokens are split and the fp32 partial
-// tiles are summed in a fixed order by a second kernel (deterministic, no atomics).
-// fp32 inputs use a plain FMA tile kernel (small layers only).
+// The tokens are split into slices (about 2048 workgroups in all); every workgroup writes
+// its fp32 tile to a partial buffer, and a second kernel sums the slices in a fixed order
+// (deterministic, no atomics) and adds twice the sum to H and its mirror, so H is exactly
+// symmetric.  fp32 inputs use a plain FMA tile kernel (small layers only).
 //
 // The fp64 diagonal key 2 * sum_t x^2 (exact products, fp64 sums) decides the ActOrder
 // permutation, where fp32 sums are not precise enough to order nearly equal channels
-// reproducibly.  For 16-bit inputs the diagonal-tile workgroups accumulate it from the
-// LDS stages they already hold; fp32 inputs use a separate kernel.  Per-slice fp64
-// partials are summed in a fixed order.
+// reproducibly.  A separate memory-bound kernel accumulates it (for 16-bit inputs on the
+// side stream, next to the SYRK); per-slice fp64 partials are summed in a fixed order.
 #include <algorithm>
 
 #include "common.h"
