@@ -105,7 +105,8 @@ struct SideStream {
 std::mutex& side_mutex();
 gptq_status side_stream(SideStream** out);   // of the current device
 
-// fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C (row-major, batched by blockIdx.z).
+// fp32-accurate matrix-core GEMM: C = alpha * op(A) op(B) + beta * C (row-major, batched by
+// blockIdx.z); large products as split-bf16 products, small ones on the fp32 instruction.
 struct GemmArgs {
   int M, N, K;
   const float* A; int64_t lda, sA;   // A [M, K]

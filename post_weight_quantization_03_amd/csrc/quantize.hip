@@ -17,7 +17,8 @@
 //                    (processing order), the group scale/zero, and the block's columns
 //                    of Err.
 //     lazy update:   hierarchical (see sweep_range): W_p[:, right] -= Err[:, left] @ U[left,
-//                    right] on the fp32 matrix cores, Err [d_out, d_in] in processing order.
+//                    right] as fp32-accurate matrix-core products (split-bf16 when large),
+//                    Err [d_out, d_in] in processing order.
 //   unpermute:       codes back to original column order; g_idx.
 #include <type_traits>
 #include <utility>
