@@ -19,7 +19,8 @@
 // The fp64 diagonal key 2 * sum_t x^2 (exact products, fp64 sums) decides the ActOrder
 // permutation, where fp32 sums are not precise enough to order nearly equal channels
 // reproducibly.  A separate memory-bound kernel accumulates it (for 16-bit inputs on the
-// side stream, next to the SYRK); per-slice fp64 partials are summed in a fixed order.
+// side stream, after the SYRK and next to its reduction); per-slice fp64 partials are
+// summed in a fixed order.
 #include <algorithm>
 
 #include "common.h"
@@ -597,21 +598,14 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
   const dim3 blk(256);
   const dim3 egrid((d_in + 256 * (mfma ? 8 : 4) - 1) / (256 * (mfma ? 8 : 4)), pl.esplit, batch);
   if (mfma) {
-    // The fp64 channel energies (memory-bound) run on the side stream next to the SYRK
-    // (matrix-core bound); the main stream joins them before the energy reduction.
+    // The fp64 channel energies (memory-bound) run on the side stream once the SYRK is done,
+    // next to the partial-tile reduction; the main stream joins them before the energy
+    // reduction.  Run concurrently with the SYRK, their reads of X slowed it by more than
+    // they cost alone (mlp_down: Hessian 54.4 -> 53.1 ms when run after it).
     std::lock_guard<std::mutex> lk(side_mutex());
     SideStream* ss = nullptr;
     if (const gptq_status st = side_stream(&ss); st != GPTQ_OK) return st;
-    GPTQ_HIP_TRY(hipEventRecord(ss->fork, stream));
-    GPTQ_HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
-    if (x_dtype == GPTQ_F16) {
-      GPTQ_LAUNCH(channel_energy_kernel<F16>, egrid, blk, 0, ss->s, static_cast<const F16*>(X), ldx, bsx, n_tokens,
-                  d_in, pl.echunk, epart);
-    } else {
-      GPTQ_LAUNCH(channel_energy_kernel<BF16>, egrid, blk, 0, ss->s, static_cast<const BF16*>(X), ldx, bsx,
-                  n_tokens, d_in, pl.echunk, epart);
-    }
-    GPTQ_HIP_TRY(hipEventRecord(ss->join, ss->s));
+
 
     const dim3 sblk(64 * SYRK_WAVES);
     const dim3 grid(pl.ntiles * pl.ksplit, batch);
@@ -631,6 +625,16 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
                   partial, pl.ntiles);
     }
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
+    GPTQ_HIP_TRY(hipEventRecord(ss->fork, stream));
+    GPTQ_HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
+    if (x_dtype == GPTQ_F16) {
+      GPTQ_LAUNCH(channel_energy_kernel<F16>, egrid, blk, 0, ss->s, static_cast<const F16*>(X), ldx, bsx, n_tokens,
+                  d_in, pl.echunk, epart);
+    } else {
+      GPTQ_LAUNCH(channel_energy_kernel<BF16>, egrid, blk, 0, ss->s, static_cast<const BF16*>(X), ldx, bsx,
+                  n_tokens, d_in, pl.echunk, epart);
+    }
+    GPTQ_HIP_TRY(hipEventRecord(ss->join, ss->s));
     GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
                 H, bsh);
     GPTQ_HIP_TRY(hipStreamWaitEvent(stream, ss->join, 0));
