@@ -534,17 +534,31 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
   pl.ksplit = 1;
   pl.kchunk = n_tokens;
   if (mfma) {
-    // about 2048 workgroups (8 per CU): shorter token slices balance the CUs better than
-    // the extra partial tiles cost in the reduction
-    const int64_t want = (2048 + static_cast<int64_t>(pl.ntiles) * batch - 1) /
-                         (static_cast<int64_t>(pl.ntiles) * batch);
+    // About 2048 workgroups (8 per CU): shorter token slices balance the CUs better than
+    // the extra partial tiles cost in the reduction.  Then, among slice counts from 1/16
+    // fewer up to 64, the one with the fewest rounds x tokens per slice (one workgroup fills
+    // a CU; each partial tile costs the reduction about two tokens' worth of SYRK time): 15
+    // rather than 16 slices at 136 tiles fill 8 rounds instead of leaving a ninth half empty.
+    // Fewer slices than that never: longer fp32 accumulation chains make H less accurate.
+    const int64_t tiles = static_cast<int64_t>(pl.ntiles) * batch;
+    const int64_t want = (2048 + tiles - 1) / tiles;
     const int64_t cap = std::max<int64_t>(1, n_tokens / kMinTokensPerSplit);
-    pl.ksplit = static_cast<int>(std::min<int64_t>(std::min(want, cap), 64));
-    pl.kchunk = (n_tokens + pl.ksplit - 1) / pl.ksplit;
-    pl.kchunk = (pl.kchunk + SBK - 1) / SBK * SBK;
-    if (pl.kchunk == 0) pl.kchunk = SBK;
-    pl.ksplit = static_cast<int>((n_tokens + pl.kchunk - 1) / pl.kchunk);
-    if (pl.ksplit < 1) pl.ksplit = 1;
+    const int64_t base = std::min<int64_t>(std::min(want, cap), 64);
+    const int n_cu = 256;
+    double best = -1.0;
+    for (int64_t k = std::max<int64_t>(1, base - base / 16); k <= 64; ++k) {
+      int64_t chunk = (n_tokens + k - 1) / k;
+      chunk = std::max<int64_t>(SBK, (chunk + SBK - 1) / SBK * SBK);
+      if (k > base && chunk < kMinTokensPerSplit) break;
+      const int64_t ks = (n_tokens + chunk - 1) / chunk;
+      const int64_t rounds = (tiles * ks + n_cu - 1) / n_cu;
+      const double cost = static_cast<double>(rounds) * static_cast<double>(chunk) + 2.0 * static_cast<double>(ks * tiles);
+      if (best < 0.0 || cost < best) {
+        best = cost;
+        pl.kchunk = chunk;
+        pl.ksplit = static_cast<int>(std::max<int64_t>(1, ks));
+      }
+    }
   }
   // energy kernel: 16-byte loads of 16 / elem_bytes channels per thread, ~1024 workgroups,
   // at least 256 tokens per slice, at most 256 slices (their sum is one thread per channel)
