@@ -234,16 +234,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------
 // The same product on the bf16 matrix cores, at fp32 accuracy, by splitting the operands.
 // Each fp32 value is written as x = x0 + x1 + x2 with x0 = bf16(x), x1 = bf16(x - x0),
-// x2 = bf16(x - x0 - x1) (round to nearest even; every difference is exact in fp32), so
-// |x - x0 - x1 - x2| <= 2^-27 |x|.  Of the nine cross products a_i b_j the six with
-// i + j <= 2 are kept; the three dropped ones are below 2^-25 |a b| together.  Products of
-// two bf16 values are exact in fp32 and the sums are fp32, as in the fp32 kernel, so the
-// result carries fp32 rounding: the operands are never rounded to a 16-bit type as a whole.
+// x2 = bf16(x - x0 - x1) (round to nearest even, unit roundoff 2^-8 for bf16's 8-bit
+// significand; every difference is exact in fp32), so |x - x0 - x1 - x2| <= 2^-24 |x|.  Of
+// the nine cross products a_i b_j the six with i + j <= 2 are kept; the dropped ones and the
+// two residuals change a product by at most about 2^-22 |a b|, the order of the fp32
+// roundings of the accumulation itself.  Products of two bf16 values are exact in fp32 and
+// the sums are fp32, as in the fp32 kernel: the operands are never rounded to a 16-bit type
+// as a whole.
 // Six v_mfma_f32_32x32x16_bf16 per 32x32x16 block run at 2500 / 6 = 417 TFLOP/s of fp32
 // products against 157 TFLOP/s for v_mfma_f32_32x32x2_f32.
 //
-// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 blocks of 32 x 32), two or
-// three workgroups per CU.  The three parts are stored in LDS as bf16 planes: A (and B^T)
+// Tile 128 x 128 x 16, 256 threads = 4 waves of 64 x 64 (2 x 2 blocks of 32 x 32), three
+// workgroups per CU.  The three parts are stored in LDS as bf16 planes: A (and B^T)
 // with K contiguous per row, 32 bytes = two 16-byte chunks per row, the chunks of rows
 // 8..15 (mod 16) swapped, so that a 16-lane read of 16 bytes per lane (rows r..r+15, one k
 // half) and a 32-lane write of 8 bytes per lane (8 whole rows) each cover all 64 banks
