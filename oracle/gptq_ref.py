@@ -7,26 +7,41 @@ or helper with that path: it receives the same seeded input bytes and nothing el
 
 It is a plain, slow, obviously-correct restatement of what the pages compute, in
 float64 throughout; library primitives used as single steps are numpy's matmul and
-Cholesky and scipy's triangular solve.  Sources (web pages, cited by title and
-section):
+Cholesky, scipy's triangular solve and BLAS rank-one update.  Sources (web pages,
+cited by title and section):
 
 * [SRS]  "Same Ruler, Smarter Placement: GPTQ" — 1.4 (H = 2XX^T), 1.5 (the
-  compensating update, Steps 1-3), 1.6 (dampening), 1.7 (the Cholesky trick and its
-  four-step recipe), 1.8 (lazy batch update), 1.9 (activation ordering).
+  compensating update of one column, Steps 1-3), 1.6 (dampening), 1.7 (the Cholesky
+  trick: the rows of the upper factor U carry the conditional updates), 1.9
+  (activation ordering), 1.11 (a symmetric grid: scale = max|w| / 7 at 4 bits).
 * [ARCH] "GPTQ Architecture, in depth" — "The algorithm in code" (Hessian hook,
-  min-max group fit, the blocked column loop, dead inputs, act-order, damping),
-  "Groups, act-order and other knobs" (g_idx), "Packing, tooling and serving".
+  dead inputs, act-order, damping, asymmetric min-max group grid refitted at each
+  group start), "Groups, act-order and other knobs" (g_idx, symmetric grids, static
+  groups), "Packing, tooling and serving".
 * [LIN]  "04 — GPTQ: Hessian-Weighted Rounding, the OBS Lineage, and Why It Still
   Ships" — section 1 (objective ||WX - What X||_F^2), section 8 (bit-level layout).
 * [ACT]  "GPTQ > ActOrder: Activation-Based Column Ordering" (descending diagonal).
 
+The sweep is the unblocked column-by-column form of [SRS] 1.5: every column's
+scaled error reaches all later columns immediately.  The pages' lazy batches of 128
+columns ([SRS] 1.8) only change when those updates land, so the unblocked form is the
+plain definition the blocked GPU sweep must reproduce.
+
 Readings where the pages are silent or disagree (all listed with reasons in the
 design notes of the repository):
 
-* Rounding is round-half-to-even (numpy ``rint``), as the listing's ``torch.round``;
-  the hand example's "half away from zero" remark concerns a test-only grid.
+* Rounding is round-half-to-even (numpy ``rint``), as the listing's ``torch.round``,
+  and a code is the rounded quotient plus the zero point, clamped
+  (clamp(round(w / scale) + zero)); the hand example's "half away from zero" remark
+  concerns a test-only grid.
 * ``group_size = -1`` means one grid per row, fitted once at the first column on the
   whole (dead-zeroed, permuted) row.
+* Symmetric grid: the zero point is the middle level 2^(bits-1) and the scale is
+  max|w| / (2^(bits-1) - 1), the grid of [SRS] 1.11 (max|w| / 7 at 4 bits) stored
+  with an unsigned code.
+* Static groups: the groups are runs of consecutive ORIGINAL columns and each group's
+  grid is fitted on the dead-zeroed weights before the sweep; every column is
+  quantized on the grid of its original group, whatever its processing position.
 * ActOrder sorts by the fp64 Hessian diagonal after the dead-input fix, descending,
   ties broken by ascending original index (a stable sort).
 * The damping mean is taken over the diagonal after the dead-input fix.
@@ -35,9 +50,10 @@ design notes of the repository):
 
 Pins (tests/test_oracle_*.py): brute-force H on tiny integer inputs, closed-form
 2x2 factor, Schur-complement downdates, damping bounds, an independent explicit-
-inverse OBS solver, an independent Babai nearest-plane solver, the diagonal-H =>
-round-to-nearest invariant, block-size and H-scale invariance, the page's 4x4
-worked example, and the page's checkpoint byte formula.
+inverse OBS solver, an independent Babai nearest-plane solver, an independent
+lazy-batch (blocked) sweep, the diagonal-H => round-to-nearest invariant, an exact
+rounding tie, H-scale invariance, the page's 4x4 worked example, and the page's
+checkpoint byte formula.
 """
 
 from __future__ import annotations
@@ -46,12 +62,13 @@ import dataclasses
 
 import numpy as np
 from scipy.linalg import solve_triangular
+from scipy.linalg.blas import dger
 
 __all__ = [
     "NotSPD", "widen", "ref_accumulate_hessian", "ref_channel_energy", "ref_hessian_entries",
-    "ref_column_order", "ref_prepare_hinv", "fit_minmax",
-    "gptq_sweep", "MinMaxGrid", "ref_quantize_layer", "ref_dequantize",
-    "ref_layer_loss", "ref_pack_int4", "ref_unpack_int4", "ref_gptq_layer",
+    "ref_column_order", "ref_prepare_hinv", "UniformGrid", "obs_sweep", "GridDecisions",
+    "ref_quantize_layer", "ref_dequantize", "ref_layer_loss", "ref_pack_int4", "ref_unpack_int4",
+    "ref_gptq_layer",
 ]
 
 
@@ -62,10 +79,12 @@ class NotSPD(Exception):
 # ----------------------------------------------------------------------------- inputs
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact widening of stored inputs to float64 (bf16 bit patterns or fp32)."""
+    """Exact widening of stored inputs to float64 (bf16 or fp16 bit patterns, or fp32)."""
     if dtype == "bf16":
         bits = np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     raise ValueError(dtype)
@@ -100,11 +119,14 @@ def ref_channel_energy(X: np.ndarray, dtype: str, rows_per_step: int = 8192) -> 
     e = torch.zeros(d, dtype=torch.float64)
     for t0 in range(0, n, rows_per_step):
         slab = np.ascontiguousarray(X[t0:t0 + rows_per_step])
-        if dtype == "bf16":
-            # exact widening of the bf16 bits to fp32; a bf16 value has 8 significant bits,
-            # so its square is exact in fp32, and the sum runs in fp64
-            bits = torch.from_numpy(slab.view(np.int16)).to(torch.int32).bitwise_and(0xFFFF)
-            x = torch.bitwise_left_shift(bits, 16).view(torch.float32)
+        if dtype in ("bf16", "f16"):
+            # exact widening to fp32; a 16-bit value has at most 11 significant bits, so
+            # its square is exact in fp32, and the sum runs in fp64
+            if dtype == "bf16":
+                bits = torch.from_numpy(slab.view(np.int16)).to(torch.int32).bitwise_and(0xFFFF)
+                x = torch.bitwise_left_shift(bits, 16).view(torch.float32)
+            else:
+                x = torch.from_numpy(slab.view(np.float16)).to(torch.float32)
             e += 2.0 * (x * x).sum(dim=0, dtype=torch.float64)
         else:
             x = torch.from_numpy(widen(slab, dtype))
@@ -174,72 +196,107 @@ def ref_prepare_hinv(H: np.ndarray, damp: float = 0.01, act_order: bool = False)
     return dict(U=U, perm=perm, dead=dead, lam=lam, Hp=Hp)
 
 
-# --------------------------------------------------------------- grid ([ARCH] fit_group)
+# ----------------------------------------------------------- the quantization grid
 
-def fit_minmax(Wg: np.ndarray, maxq: int):
-    """Asymmetric min-max grid of each row of Wg: (scale, zero) per row.
+@dataclasses.dataclass(frozen=True)
+class UniformGrid:
+    """A grid of 2^bits equally spaced levels, one per row of a weight segment.
 
-    The range always contains 0: lo = min(0, min row), hi = max(0, max row);
-    scale = max((hi - lo) / maxq, 1e-8); zero = round(-lo / scale).
-    Returns also the pre-rounding zero value -lo/scale (for the replay check).
+    A weight w is represented by the level ``code`` in [0, maxq] as
+    What = scale * (code - zero).
+
+    Asymmetric ([ARCH] "The algorithm in code"): the levels cover the segment's range
+    widened to contain 0, [lo, hi] = [min(0, min w), max(0, max w)], so the step is
+    (hi - lo) / maxq (never below 1e-8) and the level of 0 is -lo / step rounded.
+    Symmetric ([ARCH] "Groups, act-order and other knobs"; the grid of [SRS] 1.11):
+    the step is max|w| / (2^(bits-1) - 1) (never below 1e-8) and 0 sits at the fixed
+    middle level 2^(bits-1).
     """
-    lo = np.minimum(Wg.min(axis=1), 0.0)
-    hi = np.maximum(Wg.max(axis=1), 0.0)
-    scale = np.maximum((hi - lo) / maxq, 1e-8)
-    zval = -lo / scale
-    return scale, np.rint(zval), zval
+
+    bits: int
+    sym: bool = False
+
+    @property
+    def maxq(self) -> int:
+        return 2 ** self.bits - 1
+
+    def fit(self, seg: np.ndarray):
+        """Per row of ``seg`` [rows, k]: (scale, zero, zero before rounding)."""
+        if self.sym:
+            half = 2 ** (self.bits - 1)
+            scale = np.maximum(np.max(np.abs(seg), axis=1) / (half - 1), 1e-8)
+            zero = np.full(seg.shape[0], float(half))
+            return scale, zero, zero.copy()
+        lo = np.minimum(seg.min(axis=1), 0.0)
+        hi = np.maximum(seg.max(axis=1), 0.0)
+        scale = np.maximum((hi - lo) / self.maxq, 1e-8)
+        zero_pre = -lo / scale
+        return scale, np.rint(zero_pre), zero_pre
+
+    def code(self, w: np.ndarray, scale: np.ndarray, zero: np.ndarray):
+        """(code, value before rounding in level units) of each weight: the quotient
+        w / scale is rounded to the nearest integer (ties to even), the zero point is
+        added, and the result is clamped to [0, maxq]."""
+        quot = w / scale
+        return np.clip(np.rint(quot) + zero, 0, self.maxq), quot + zero
 
 
-# -------------------------------------------------- column sweep ([SRS] 1.5, 1.7, 1.8)
+# -------------------------------------------- column sweep ([SRS] 1.5 and 1.7, unblocked)
 
-def gptq_sweep(Wp: np.ndarray, U: np.ndarray, block: int, quantize_column) -> np.ndarray:
-    """Blocked GPTQ sweep over the columns of Wp (modified in place).
+def obs_sweep(Wp: np.ndarray, U: np.ndarray, quantize_column) -> np.ndarray:
+    """GPTQ over the columns of Wp [rows, cols] in order; Wp is modified in place.
 
-    For each column q in order: the grid turns the current column into What_q
-    (``quantize_column(q, Wp)``); err_q = (W_q - What_q) / U_qq; the columns after q
-    inside the current block absorb err_q * U[q, q+1:] at once ([SRS] 1.5 Step 3 with
-    the rows of U from 1.7); the errors of a finished block are applied to every
-    later column in one product Err @ U[block, later] ([SRS] 1.8 lazy batch update,
-    which only changes when updates land, not which).  Returns What [rows, cols].
+    For column q ([SRS] 1.5, Steps 1-3, with the conditional inverse read off the rows of
+    the upper factor U, [SRS] 1.7): the current column becomes What_q =
+    ``quantize_column(q, Wp)``; its error scaled by the conditional inverse diagonal,
+    delta_q = (Wp_q - What_q) / U_qq, is taken out of every later column at once,
+    Wp[:, j] -= delta_q * U[q, j] for j > q.  The rank-one update is one BLAS call on a
+    column-major copy.  Returns What [rows, cols].
     """
     rows, cols = Wp.shape
-    What = np.zeros_like(Wp)
-    for i in range(0, cols, block):
-        j2 = min(i + block, cols)
-        Err = np.zeros((rows, j2 - i))
-        for q in range(i, j2):
-            What[:, q] = quantize_column(q, Wp)
-            err = (Wp[:, q] - What[:, q]) / U[q, q]
-            Wp[:, q + 1:j2] -= np.outer(err, U[q, q + 1:j2])
-            Err[:, q - i] = err
-        if j2 < cols:
-            Wp[:, j2:] -= Err @ U[i:j2, j2:]
+    Wf = np.asfortranarray(Wp, dtype=np.float64)
+    What = np.zeros((rows, cols))
+    for q in range(cols):
+        What[:, q] = quantize_column(q, Wf)
+        delta = (Wf[:, q] - What[:, q]) / U[q, q]
+        if q + 1 < cols:
+            later = Wf[:, q + 1:]
+            out = dger(-1.0, delta, np.ascontiguousarray(U[q, q + 1:]), a=later, overwrite_a=1)
+            if not np.shares_memory(out, later):   # BLAS had to copy: write it back
+                later[...] = out
+    Wp[...] = Wf
     return What
 
 
 @dataclasses.dataclass
-class MinMaxGrid:
-    """Per-row (group_size=-1) or per-group asymmetric grid of [ARCH] "The algorithm
-    in code": at the first column of every group the grid is refitted on the current
-    (already compensated) weights of that group; codes are
-    q = clamp(round(w / scale) + zero, 0, 2^bits - 1) and What = scale * (q - zero).
+class GridDecisions:
+    """The grid decisions of one sweep ([ARCH] "The algorithm in code" and "Groups,
+    act-order and other knobs"), as the per-column callback of :func:`obs_sweep`.
 
-    With ``forced_codes`` / ``forced_zeros`` (permuted column order) the decisions are
-    taken from the caller instead (teacher-forced replay); every place where the
-    forced integer differs from this oracle's own rounding is recorded together with
-    the distance of the oracle's pre-rounding value from the midpoint between the
-    two integers.
+    Per-row (group_size = -1): one grid per row, fitted at column 0 on the whole row.
+    Groups: the grid of the group of g consecutive processing positions is refitted on
+    the current (already compensated) weights at the group's first position.  Static
+    groups: ``static_fit`` holds (scale, zero, zero before rounding) of every group of
+    g consecutive ORIGINAL columns, fitted before the sweep; processing position q uses
+    the grid of group perm[q] // g.
+
+    With ``forced_codes`` / ``forced_zeros`` (processing order; zeros per stored group)
+    the integer decisions are taken from the caller instead (teacher-forced replay);
+    every place where a forced integer differs from this oracle's own rounding is
+    recorded with the distance of the oracle's value before rounding from the midpoint
+    between the two integers.
     """
 
     rows: int
     cols: int
-    bits: int
+    grid: UniformGrid
     group_size: int
+    perm: np.ndarray | None = None
+    static_fit: tuple | None = None
     forced_codes: np.ndarray | None = None
     forced_zeros: np.ndarray | None = None
 
     def __post_init__(self):
-        self.maxq = 2 ** self.bits - 1
         self.g = self.cols if self.group_size == -1 else self.group_size
         self.n_groups = -(-self.cols // self.g)
         self.codes = np.zeros((self.rows, self.cols), dtype=np.int64)
@@ -249,63 +306,82 @@ class MinMaxGrid:
         self.zero_pre = np.zeros((self.n_groups, self.rows))
         self.code_div = []     # (row, col, |v - midpoint|, |code_a - code_b|)
         self.zero_div = []     # (group, row, |v - midpoint|, |zero_a - zero_b|)
-        self._scale = self._zero = None
+        self._cur = None
+        if self.static_fit is not None:
+            for gi in range(self.n_groups):
+                s, z, zp = (np.asarray(a[gi], dtype=np.float64) for a in self.static_fit)
+                self._set_group(gi, s, z, zp)
 
     @staticmethod
-    def _midpoint_gap(v, a, b):
+    def _gap(v, a, b):
         return np.abs(v - 0.5 * (a + b)), np.abs(a - b)
 
-    def __call__(self, q: int, Wp: np.ndarray) -> np.ndarray:
-        if q % self.g == 0:
+    def _set_group(self, gi, scale, zero, zero_pre):
+        if self.forced_zeros is not None and not self.grid.sym:
+            fz = self.forced_zeros[gi].astype(np.float64)
+            bad = np.nonzero(fz != zero)[0]
+            gap, dist = self._gap(zero_pre[bad], zero[bad], fz[bad])
+            self.zero_div += [(gi, int(r), float(g_), float(d_)) for r, g_, d_ in zip(bad, gap, dist)]
+            zero = fz
+        self.scales[gi], self.zeros[gi], self.zero_pre[gi] = scale, zero, zero_pre
+
+    def __call__(self, q: int, Wf: np.ndarray) -> np.ndarray:
+        if self.static_fit is not None:
+            gi = int(self.perm[q]) // self.g
+        else:
             gi = q // self.g
-            scale, zero, zval = fit_minmax(Wp[:, q:q + self.g], self.maxq)
-            if self.forced_zeros is not None:
-                fz = self.forced_zeros[gi].astype(np.float64)
-                bad = np.nonzero(fz != zero)[0]
-                gap, dist = self._midpoint_gap(zval[bad], zero[bad], fz[bad])
-                self.zero_div += [(gi, int(r), float(g_), float(d_)) for r, g_, d_ in zip(bad, gap, dist)]
-                zero = fz
-            self._scale, self._zero = scale, zero
-            self.scales[gi], self.zeros[gi], self.zero_pre[gi] = scale, zero, zval
-        v = Wp[:, q] / self._scale + self._zero
-        code = np.clip(np.rint(v), 0, self.maxq)
+            if q % self.g == 0:
+                self._set_group(gi, *self.grid.fit(Wf[:, q:q + self.g]))
+        scale, zero = self.scales[gi], self.zeros[gi].astype(np.float64)
+        code, v = self.grid.code(Wf[:, q], scale, zero)
         if self.forced_codes is not None:
             fc = self.forced_codes[:, q].astype(np.float64)
             bad = np.nonzero(fc != code)[0]
-            gap, dist = self._midpoint_gap(v[bad], code[bad], fc[bad])
+            gap, dist = self._gap(v[bad], code[bad], fc[bad])
             self.code_div += [(int(r), q, float(g_), float(d_)) for r, g_, d_ in zip(bad, gap, dist)]
             code = fc
         self.pre[:, q] = v
         self.codes[:, q] = code
-        return self._scale * (code - self._zero)
+        return scale * (code - zero)
 
 
 def ref_quantize_layer(W: np.ndarray, dtype: str, prep: dict, bits: int = 4,
-                       group_size: int = 128, block_size: int = 128,
+                       group_size: int = 128, sym: bool = False, static_groups: bool = False,
                        forced_codes: np.ndarray | None = None,
                        forced_zeros: np.ndarray | None = None):
     """GPTQ of one layer given the output of :func:`ref_prepare_hinv`.
 
     W [d_out, d_in] (stored dtype) -> codes [d_out, d_in] in ORIGINAL column order,
-    scales / zeros [n_groups, d_out] (groups formed in processing order), g_idx
-    [d_in] (group of each original column, [ARCH] "Groups, act-order and other
-    knobs"), perm, and the dequantized What in original order.
+    scales / zeros [n_groups, d_out], g_idx [d_in] (group of each original column,
+    [ARCH] "Groups, act-order and other knobs"), perm, and the dequantized What in
+    original order.  Groups are runs of processing positions, or of original columns
+    with ``static_groups`` (fitted before the sweep on the dead-zeroed W).
     ``forced_codes`` (original order) / ``forced_zeros`` switch on the replay.
     """
     U, perm, dead = prep["U"], prep["perm"], prep["dead"]
     Wf = widen(W, dtype)
     rows, cols = Wf.shape
     Wf[:, dead] = 0.0
+    grid = UniformGrid(bits, sym)
+    static = static_groups and group_size != -1
+    static_fit = None
+    if static:
+        fits = [grid.fit(Wf[:, c:c + group_size]) for c in range(0, cols, group_size)]
+        static_fit = tuple(np.array([f[i] for f in fits]) for i in range(3))
     Wp = Wf[:, perm].copy()
     fc = None if forced_codes is None else np.asarray(forced_codes)[:, perm]
-    grid = MinMaxGrid(rows, cols, bits, group_size, fc, forced_zeros)
-    What_p = gptq_sweep(Wp, U, block_size, grid)
+    dec = GridDecisions(rows, cols, grid, group_size, perm=perm, static_fit=static_fit, forced_codes=fc,
+                        forced_zeros=forced_zeros)
+    What_p = obs_sweep(Wp, U, dec)
     inv = np.empty_like(perm)
     inv[perm] = np.arange(cols)
-    codes = grid.codes[:, inv].astype(np.uint8)
-    g_idx = (inv // grid.g).astype(np.int32)
-    return dict(codes=codes, scales=grid.scales, zeros=grid.zeros.astype(np.uint8),
-                g_idx=g_idx, perm=perm, What=What_p[:, inv], grid=grid)
+    codes = dec.codes[:, inv].astype(np.uint8)
+    if static:
+        g_idx = (np.arange(cols) // group_size).astype(np.int32)
+    else:
+        g_idx = (inv // dec.g).astype(np.int32)
+    return dict(codes=codes, scales=dec.scales, zeros=dec.zeros.astype(np.uint8),
+                g_idx=g_idx, perm=perm, What=What_p[:, inv], grid=dec)
 
 
 def ref_dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
@@ -367,8 +443,8 @@ def ref_unpack_int4(qweight: np.ndarray, qzeros: np.ndarray):
 # ------------------------------------------------------------------- whole layer
 
 def ref_gptq_layer(W: np.ndarray, X_chunks, dtype: str, bits: int = 4, group_size: int = 128,
-                   block_size: int = 128, damp: float = 0.01, act_order: bool = False,
-                   timings: dict | None = None):
+                   damp: float = 0.01, act_order: bool = False, sym: bool = False,
+                   static_groups: bool = False, timings: dict | None = None):
     """Hessian -> prepare -> quantize for one layer; ``X_chunks`` is an iterable of
     token-major activation slabs.  Per-stage wall times go to ``timings``."""
     import time
@@ -381,7 +457,7 @@ def ref_gptq_layer(W: np.ndarray, X_chunks, dtype: str, bits: int = 4, group_siz
     t1 = time.perf_counter()
     prep = ref_prepare_hinv(H, damp, act_order)
     t2 = time.perf_counter()
-    res = ref_quantize_layer(W, dtype, prep, bits, group_size, block_size)
+    res = ref_quantize_layer(W, dtype, prep, bits, group_size, sym, static_groups)
     t3 = time.perf_counter()
     if timings is not None:
         timings.update(hessian=t1 - t0, prepare=t2 - t1, quantize=t3 - t2)

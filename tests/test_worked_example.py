@@ -3,7 +3,7 @@
 Fixture: tests/golden/worked_example_4x4.json ("Same Ruler, Smarter Placement:
 GPTQ", sections 1.11 and 2).  The page's grid is symmetric per input column with
 scale max|column| / 7; it is used here as a test-only grid through the oracle's
-generic sweep.  The page compensates with unconditioned rows of its inverse, which
+generic sweep (the page's scale max|w| / 7 with codes in [-8, 7]).  The page compensates with unconditioned rows of its inverse, which
 coincides with GPTQ for the first column only, so the checks are: the column-0 step,
 the codes of columns 0-2 (which the conditional procedure reproduces), the RTN and
 naive per-tensor losses, and the true output y.
@@ -44,8 +44,8 @@ def test_column_zero_step_and_first_codes():
     codes = {}
     Wp = W.copy()
     quant = sym_column_grid(codes)
-    # one column of the sweep, by hand through the oracle's block machinery (block=1)
-    R.gptq_sweep(Wp[:, :1].copy(), U[:1, :1], 1, quant)   # fills codes[0]
+    # the first column through the oracle's sweep (a one-column problem)
+    R.obs_sweep(Wp[:, :1].copy(), U[:1, :1], quant)   # fills codes[0]
     Wstep = W.copy()
     Wq0 = np.array(codes[0]) * np.max(np.abs(W[:, 0])) / 7.0
     err = (W[:, 0] - Wq0) / U[0, 0]
@@ -54,7 +54,7 @@ def test_column_zero_step_and_first_codes():
     np.testing.assert_allclose(Wstep, FIX["W_after_col0"], atol=2e-4)
     # full conditional sweep: the first three columns keep the page's codes
     codes = {}
-    R.gptq_sweep(W.copy(), U, 4, sym_column_grid(codes))
+    R.obs_sweep(W.copy(), U, sym_column_grid(codes))
     assert [codes[0], codes[1], codes[2]] == FIX["codes_cols_0_1_2"]
 
 
