@@ -56,20 +56,34 @@ typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
 /* Quantizer knobs ("GPTQ Architecture, in depth", "The algorithm in code" and
  * "Groups, act-order and other knobs"; damping: "Same Ruler, Smarter Placement:
  * GPTQ", 1.6).
- *   bits        2..8; codes lie in [0, 2^bits - 1]
- *   group_size  -1: one asymmetric min-max grid per row, fitted once on the whole row;
- *               otherwise a divisor of 128 that divides d_in: the grid of each group of
- *               consecutive columns IN PROCESSING ORDER is refitted on the current
- *               (already compensated) weights when the sweep reaches its first column
- *   block_size  columns per lazy batch; must be 128
- *   damp        lambda = damp * mean(diag H) is added to the diagonal (>= 0)
- *   act_order   nonzero: process columns by descending Hessian diagonal            */
+ *   bits          2..8; codes lie in [0, 2^bits - 1]
+ *   group_size    -1: one grid per row, fitted once on the whole row; otherwise 16, 32,
+ *                 64 or 128 dividing d_in: the grid of each group of consecutive
+ *                 columns IN PROCESSING ORDER is refitted on the current (already
+ *                 compensated) weights when the sweep reaches its first column
+ *   block_size    columns per lazy batch; must be 128
+ *   damp          lambda = damp * mean(diag H) is added to the diagonal (>= 0)
+ *   act_order     nonzero: process columns by descending Hessian diagonal
+ *   sym           0: asymmetric min-max grid, scale = (hi - lo) / maxq with
+ *                 [lo, hi] = [min(0, min w), max(0, max w)], zero = rne(-lo / scale);
+ *                 nonzero: symmetric grid, scale = max|w| / (2^(bits-1) - 1), zero fixed
+ *                 at the middle level 2^(bits-1) (the grid of "Same Ruler, Smarter
+ *                 Placement: GPTQ", 1.11, stored with an unsigned code); scales are never
+ *                 below 1e-8 ("Groups, act-order and other knobs": symmetric or asymmetric)
+ *   static_groups nonzero (with group_size > 0): groups are runs of group_size
+ *                 consecutive ORIGINAL columns, each fitted once on the dead-zeroed W
+ *                 before the sweep; every column is quantized on its original group's grid
+ *                 wherever act_order puts it, and g_idx[c] = c / group_size ("Groups,
+ *                 act-order and other knobs": static groups keep the scale reads of the
+ *                 serving kernel contiguous)                                               */
 typedef struct {
   int bits;
   int group_size;
   int block_size;
   float damp;
   int act_order;
+  int sym;
+  int static_groups;
 } gptq_params;
 
 /* Which call a workspace is sized for. */
@@ -132,8 +146,8 @@ gptq_status gptq_prepare_hinv(int batch, int d_in, const float* H, int64_t batch
  *
  * For every problem e, with W_p = W[:, perm] in fp32 and dead columns zeroed:
  *   for each column j in processing order:
- *     at a group start: scale = max((hi - lo) / maxq, 1e-8), zero = rne(-lo / scale)
- *       with lo = min(0, min W_p[r, group]), hi = max(0, max W_p[r, group]) per row
+ *     at a group start (not with static groups): the grid of the params above is fitted
+ *       per row on the current values of the group's columns
  *     code = clamp(rne(W_p[r, j] / scale) + zero, 0, maxq)
  *     err  = (W_p[r, j] - scale * (code - zero)) / U[j, j]
  *     W_p[r, later columns of the block] -= err * U[j, later columns of the block]
@@ -141,7 +155,8 @@ gptq_status gptq_prepare_hinv(int batch, int d_in, const float* H, int64_t batch
  * Outputs (rne = round half to even):
  *   codes  uint8 [d_out, d_in] in ORIGINAL column order (batch stride d_out*d_in)
  *   scales fp32 [n_groups, d_out], zeros uint8 [n_groups, d_out]; n_groups = d_in /
- *          group_size, or 1 per row; group g holds processing positions [g*gs, (g+1)*gs)
+ *          group_size, or 1 per row; group g holds processing positions [g*gs, (g+1)*gs),
+ *          or original columns [g*gs, (g+1)*gs) with static groups
  *   g_idx  int32 [d_in]: group of each original column (0 per row)
  * W is bf16, fp16 or fp32 with row stride ldw and batch stride batch_stride_w; U, perm
  * and dead are the outputs of gptq_prepare_hinv (U batch stride batch_stride_u).
@@ -176,15 +191,27 @@ gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const u
 size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
                            int64_t n_tokens_hint, const gptq_params* p);
 
-/* Measurement hook for the Hessian SYRK kernel (the dominant kernel of the path).
- * While enabled (on != 0), every gptq_accumulate_hessian call records a pair of HIP events
- * on its stream immediately around its SYRK kernel launch (the matrix-core kernel for
- * bf16/fp16 inputs, the vector-ALU kernel for fp32 inputs).  gptq_timing_read waits for the
- * recorded events, returns the summed elapsed milliseconds and the number of launches since
- * the previous read, and forgets them.  Events are created by the library on first use and
- * reused; the hook is process-wide and not meant for concurrent callers. */
+/* Measurement hook for the kernels the roofline figures are quoted on.
+ *   GPTQ_TIME_SYRK       the Hessian SYRK kernel of gptq_accumulate_hessian (the matrix-core
+ *                        kernel for bf16/fp16 inputs, the vector-ALU kernel for fp32 inputs)
+ *   GPTQ_TIME_LAZY_GEMM  every lazy trailing-update product of gptq_quantize_layer
+ *   GPTQ_TIME_SWEEP      every 128-column sweep kernel of gptq_quantize_layer
+ *   GPTQ_TIME_PACK       the packing kernels of one gptq_pack_int4 call (one pair per call)
+ * While enabled (on != 0), every such launch is bracketed by a pair of HIP events recorded
+ * on the call's stream immediately around it.  gptq_timing_read waits for the recorded
+ * events of one class, returns their summed elapsed milliseconds and the number of
+ * bracketed launches since the previous read of that class, and forgets them.  Events are
+ * created by the library on first use and reused; the hook is process-wide and not meant
+ * for concurrent callers.  Returns GPTQ_ERR_INVALID_ARG for an unknown class or null
+ * outputs. */
+typedef enum {
+  GPTQ_TIME_SYRK = 0,
+  GPTQ_TIME_LAZY_GEMM = 1,
+  GPTQ_TIME_SWEEP = 2,
+  GPTQ_TIME_PACK = 3
+} gptq_timed_kernel;
 gptq_status gptq_timing_enable(int on);
-gptq_status gptq_timing_read(double* total_ms, int64_t* launches);
+gptq_status gptq_timing_read(gptq_timed_kernel which, double* total_ms, int64_t* launches);
 
 /* Static description of a status code. */
 const char* gptq_status_string(gptq_status s);

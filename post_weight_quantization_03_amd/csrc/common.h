@@ -90,9 +90,10 @@ gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uin
                          const float* scales, const uint8_t* zeros, int32_t* qweight, int32_t* qzeros,
                          uint16_t* scales_f16, hipStream_t stream);
 
-// SYRK launch timing (gptq_timing_enable / gptq_timing_read): returns the event pair to
-// record around the next SYRK launch, or nulls when timing is off.
-void timing_pair(hipEvent_t* start, hipEvent_t* stop);
+// Launch timing (gptq_timing_enable / gptq_timing_read): returns the event pair to record
+// around the next launch of the given class, or nulls when timing is off.
+constexpr int kTimedKinds = 4;
+void timing_pair(gptq_timed_kernel kind, hipEvent_t* start, hipEvent_t* stop);
 
 // A second stream per device for work that can overlap the caller's stream; two events
 // fork work onto it and join it back.  Created on first use, kept for the life of the
@@ -119,6 +120,7 @@ struct GemmArgs {
   // optional inner batch: product z = zo * batch2 + zi sits at zo * s + zi * s2
   int batch2 = 1;
   int64_t sA2 = 0, sB2 = 0, sC2 = 0;
+  int role = 0;                      // 1: a lazy trailing update of the quantizer (see gemm.hip)
 };
 enum GemmFlags {
   kLowerOut = 1,   // C square: only tiles on or below the diagonal are computed

@@ -33,7 +33,9 @@ namespace {
 // outside the product zeroed when the stage is stored to LDS.  (Editing a loaded register
 // right after its load, as the general path does for a partial vector, makes the compiler
 // wait for every load as it is issued.)
-template <bool kTransB, int TT, bool kVec>
+// kRole: 0 for the factorization's products, 1 for the quantizer's lazy trailing updates
+// (identical code; separate instantiations so that kernel traces tell them apart).
+template <bool kTransB, int TT, bool kVec, int kRole>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int GT = TT;
   constexpr int GK = TT == 64 ? 64 : 32;
@@ -283,7 +285,7 @@ __device__ __forceinline__ void split3(const float4 v, uint2& p0, uint2& p1, uin
   p2 = make_uint2(a2, b2);
 }
 
-template <bool kTransB>
+template <bool kTransB, int kRole>
 __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   constexpr int GT = 128, GK = 16;
   constexpr int PA = GK;                       // bf16 per K-contiguous row (two 16-byte chunks)
@@ -506,18 +508,26 @@ gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   const bool big = vec4 ? tiles128 >= 256 : (tiles128 >= 512 || (g.flags == 0 && tiles128 >= 256));
   const int T = big ? 128 : 64;
   const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, nz);
+  if (g.role == 1) {   // lazy trailing updates: never transposed
+    if (g.transB) return GPTQ_ERR_UNSUPPORTED;
+    if (big && vec4) GPTQ_LAUNCH((gemm_x6_kernel<false, 1>), grid, dim3(256), 0, stream, g);
+    else if (big) GPTQ_LAUNCH((gemm_f32_kernel<false, 128, false, 1>), grid, dim3(256), 0, stream, g);
+    else if (vec4) GPTQ_LAUNCH((gemm_f32_kernel<false, 64, true, 1>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false, 1>), grid, dim3(256), 0, stream, g);
+    return GPTQ_OK;
+  }
   if (big && vec4) {
-    if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true>), grid, dim3(256), 0, stream, g);
-    else GPTQ_LAUNCH((gemm_x6_kernel<false>), grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true, 0>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_x6_kernel<false, 0>), grid, dim3(256), 0, stream, g);
   } else if (big) {
-    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128, false>), grid, dim3(256), 0, stream, g);
-    else GPTQ_LAUNCH((gemm_f32_kernel<false, 128, false>), grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 128, false, 0>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 128, false, 0>), grid, dim3(256), 0, stream, g);
   } else if (vec4) {
-    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64, true>), grid, dim3(256), 0, stream, g);
-    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, true>), grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64, true, 0>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, true, 0>), grid, dim3(256), 0, stream, g);
   } else {
-    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64, false>), grid, dim3(256), 0, stream, g);
-    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false>), grid, dim3(256), 0, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_f32_kernel<true, 64, false, 0>), grid, dim3(256), 0, stream, g);
+    else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false, 0>), grid, dim3(256), 0, stream, g);
   }
   return GPTQ_OK;
 }

@@ -30,11 +30,12 @@ gptq_status check_params(const gptq_params* p, int d_in, bool need_grid) {
   return GPTQ_OK;
 }
 
-// SYRK timing state: recorded (start, stop) pairs and a pool of reusable events.
+// Launch timing state: recorded (start, stop) pairs per kernel class and a pool of
+// reusable events.
 struct TimingState {
   std::mutex mu;
   bool on = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded, pool;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded[gptq::kTimedKinds], pool;
 };
 TimingState& timing() {
   static TimingState t;
@@ -69,11 +70,11 @@ gptq_status side_stream(SideStream** out) {
   return GPTQ_OK;
 }
 
-void timing_pair(hipEvent_t* start, hipEvent_t* stop) {
+void timing_pair(gptq_timed_kernel kind, hipEvent_t* start, hipEvent_t* stop) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);
   *start = *stop = nullptr;
-  if (!t.on) return;
+  if (!t.on || kind < 0 || kind >= kTimedKinds) return;
   std::pair<hipEvent_t, hipEvent_t> p{nullptr, nullptr};
   if (!t.pool.empty()) {
     p = t.pool.back();
@@ -81,7 +82,7 @@ void timing_pair(hipEvent_t* start, hipEvent_t* stop) {
   } else if (hipEventCreate(&p.first) != hipSuccess || hipEventCreate(&p.second) != hipSuccess) {
     return;
   }
-  t.recorded.push_back(p);
+  t.recorded[kind].push_back(p);
   *start = p.first;
   *stop = p.second;
 }
@@ -96,13 +97,15 @@ gptq_status gptq_timing_enable(int on) {
   return GPTQ_OK;
 }
 
-gptq_status gptq_timing_read(double* total_ms, int64_t* launches) {
-  if (total_ms == nullptr || launches == nullptr) return GPTQ_ERR_INVALID_ARG;
+gptq_status gptq_timing_read(gptq_timed_kernel which, double* total_ms, int64_t* launches) {
+  if (total_ms == nullptr || launches == nullptr || which < 0 || which >= gptq::kTimedKinds)
+    return GPTQ_ERR_INVALID_ARG;
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);
   double sum = 0.0;
   gptq_status st = GPTQ_OK;
-  for (auto& p : t.recorded) {
+  auto& rec = t.recorded[which];
+  for (auto& p : rec) {
     float ms = 0.0f;
     if (hipEventSynchronize(p.second) != hipSuccess || hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) {
       st = GPTQ_ERR_HIP;
@@ -111,8 +114,8 @@ gptq_status gptq_timing_read(double* total_ms, int64_t* launches) {
     t.pool.push_back(p);
   }
   *total_ms = sum;
-  *launches = static_cast<int64_t>(t.recorded.size());
-  t.recorded.clear();
+  *launches = static_cast<int64_t>(rec.size());
+  rec.clear();
   return st;
 }
 
@@ -216,6 +219,6 @@ const char* gptq_status_string(gptq_status s) {
   return "unknown status";
 }
 
-const char* gptq_version(void) { return "0.1.0"; }
+const char* gptq_version(void) { return "0.2.0"; }
 
 }  // extern "C"

@@ -629,7 +629,7 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     // stores, where an epilogue in the SYRK would add to H column by column (one 4-byte
     // read-modify-write per 128-byte line).
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    timing_pair(&ev0, &ev1);
+    timing_pair(GPTQ_TIME_SYRK, &ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
       GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
@@ -654,7 +654,7 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     GPTQ_HIP_TRY(hipStreamWaitEvent(stream, ss->join, 0));
   } else {
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    timing_pair(&ev0, &ev1);
+    timing_pair(GPTQ_TIME_SYRK, &ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream, static_cast<const float*>(X), ldx, bsx,
                 n_tokens, d_in, H, bsh);

@@ -73,10 +73,14 @@ gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uin
                          const uint8_t* zeros, int32_t* qweight, int32_t* qzeros, uint16_t* scales_f16,
                          hipStream_t stream) {
   const dim3 grid((d_out + PR - 1) / PR, (d_in + PC - 1) / PC, batch);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  timing_pair(GPTQ_TIME_PACK, &ev0, &ev1);
+  if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
   GPTQ_LAUNCH(pack_qweight_kernel, grid, dim3(256), 0, stream, codes, d_out, d_in, qweight);
   const int64_t n_meta = static_cast<int64_t>(batch) * n_groups * d_out;
   GPTQ_LAUNCH(pack_meta_kernel, dim3(static_cast<unsigned>((n_meta + 255) / 256)), dim3(256), 0, stream, scales,
               zeros, n_meta, d_out, qzeros, scales_f16);
+  if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
   return GPTQ_OK;
 }
 

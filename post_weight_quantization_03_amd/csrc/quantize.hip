@@ -10,6 +10,8 @@
 //   permute_weight:  W (bf16/fp16/fp32, original order) -> W_p fp32 [d_out, d_in] in
 //                    processing order, dead columns zeroed                 (workspace)
 //   row_grid:        per-row grid only: min/max of each whole row -> scale, zero
+//   static_grid:     static groups only: the grid of every group of original columns,
+//                    fitted on W before the sweep
 //   per block b of 128 columns:
 //     block_sweep:   16 lanes per row keep the row's 128 block columns in registers
 //                    (8 each); the column value is broadcast within the row by DPP and
@@ -114,9 +116,25 @@ __global__ __launch_bounds__(256) void inverse_perm_kernel(const int32_t* __rest
   inv[static_cast<int64_t>(e) * d_in + c] = j;
 }
 
+// Grid of one row segment from its range widened to contain 0, [lo, hi] with lo <= 0 <=
+// hi ("GPTQ Architecture, in depth", "The algorithm in code" and "Groups, act-order and
+// other knobs"): asymmetric, step (hi - lo) / maxq and zero level rne(-lo / step); or
+// symmetric, step max|w| / (2^(bits-1) - 1) and zero level fixed at 2^(bits-1) (the grid
+// of "Same Ruler, Smarter Placement: GPTQ", 1.11).  The step is never below 1e-8.
+__device__ __forceinline__ void fit_grid(float lo, float hi, float maxq, bool sym, float& s, float& z) {
+  if (sym) {
+    const float half = 0.5f * (maxq + 1.0f);
+    s = fmaxf(fmaxf(-lo, hi) / (half - 1.0f), 1e-8f);
+    z = half;
+  } else {
+    s = fmaxf((hi - lo) / maxq, 1e-8f);
+    z = rintf(-lo / s);
+  }
+}
+
 // One grid per row, fitted on the whole (dead-zeroed) row at the first column.
 __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ Wp, int d_out, int d_in,
-                                                       float maxq, float* __restrict__ scales,
+                                                       float maxq, int sym, float* __restrict__ scales,
                                                        uint8_t* __restrict__ zeros) {
   __shared__ float slo[256], shi[256];
   const int r = blockIdx.x, e = blockIdx.y;
@@ -137,10 +155,39 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const float s = fmaxf((shi[0] - slo[0]) / maxq, 1e-8f);
+    float s, z;
+    fit_grid(slo[0], shi[0], maxq, sym != 0, s, z);
     scales[static_cast<int64_t>(e) * d_out + r] = s;
-    zeros[static_cast<int64_t>(e) * d_out + r] = static_cast<uint8_t>(rintf(-slo[0] / s));
+    zeros[static_cast<int64_t>(e) * d_out + r] = static_cast<uint8_t>(z);
   }
+}
+
+// Static groups: the grid of every group of G consecutive ORIGINAL columns, fitted once on
+// the dead-zeroed W before the sweep -> scales / zeros [e][group][row].  One thread per
+// (group, row), rows fastest so that the stores are coalesced.
+template <typename T>
+__global__ __launch_bounds__(256) void static_grid_kernel(const T* __restrict__ W, int64_t ldw, int64_t bsw,
+                                                          const uint8_t* __restrict__ dead, int d_out, int d_in,
+                                                          int G, float maxq, int sym, float* __restrict__ scales,
+                                                          uint8_t* __restrict__ zeros) {
+  const int ng = d_in / G;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int e = blockIdx.y;
+  if (i >= static_cast<int64_t>(ng) * d_out) return;
+  const int r = static_cast<int>(i % d_out), gi = static_cast<int>(i / d_out);
+  const T* row = W + static_cast<int64_t>(e) * bsw + static_cast<int64_t>(r) * ldw + static_cast<int64_t>(gi) * G;
+  const uint8_t* de = dead + static_cast<int64_t>(e) * d_in + static_cast<int64_t>(gi) * G;
+  float lo = 0.0f, hi = 0.0f;
+  for (int c = 0; c < G; ++c) {
+    const float v = de[c] ? 0.0f : load_as_f32(row + c);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  float s, z;
+  fit_grid(lo, hi, maxq, sym != 0, s, z);
+  const int64_t o = (static_cast<int64_t>(e) * ng + gi) * d_out + r;
+  scales[o] = s;
+  zeros[o] = static_cast<uint8_t>(z);
 }
 
 // A row of W is spread over LPR lanes (16: one DPP row; 4: one DPP quad).  Broadcast of
@@ -186,8 +233,11 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 }
 
 // One 128-column block of the sweep.  G = group size (16, 32, 64 or 128), or 0 for the
-// per-row grid already written by row_grid_kernel.  NT threads per workgroup, LPR lanes
-// per row of W, so NT / LPR rows per workgroup.
+// per-row grid already written by row_grid_kernel.  kStatic (with G = 0): every column
+// takes the grid of its original group, perm[column] / gsz, written before the sweep by
+// static_grid_kernel; each lane loads the grids of its own columns once and the column's
+// owner broadcasts them with the column value.  sym selects the symmetric grid at group
+// starts.  NT threads per workgroup, LPR lanes per row of W, so NT / LPR rows per workgroup.
 //
 // Lane k of a row keeps the C = 128 / LPR columns LPR m + k (m = 0..C-1) in registers.
 // For column j the owner lane's value is broadcast to the row's lanes, every lane of the
@@ -200,9 +250,10 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 // a lane's update reads are contiguous, the rows of a wave read the same words, and
 // columns at or before j get a zero factor.  At a group start the grid is fitted on the
 // row's current values of the group's columns (min/max reduced over the row's lanes).
-template <int G, int NT, int LPR>
+template <int G, int NT, int LPR, bool kStatic>
 __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
                                                          int64_t bsu, int d_out, int d_in, int blk, float maxq,
+                                                         int sym, const int32_t* __restrict__ perm, int gsz,
                                                          float* __restrict__ scales, uint8_t* __restrict__ zeros,
                                                          uint8_t* __restrict__ codes_p, float* __restrict__ err) {
   constexpr int C = kBlock / LPR;   // columns per lane
@@ -213,6 +264,7 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
   constexpr int CP = LPR == 4 ? C + 4 : C;
   constexpr int UR = LPR * CP;      // floats per staged U row
   static_assert(G == 0 || G % LPR == 0, "a group spans whole registers");
+  static_assert(!kStatic || G == 0, "static groups are fitted before the sweep");
   __shared__ __attribute__((aligned(16))) float Ul[kBlock * UR];
   __shared__ float inv_d[kBlock];
   const int e = blockIdx.y;
@@ -250,11 +302,24 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
   }
   __syncthreads();
   if (!live) return;   // whole rows leave together; no barrier follows
-  const int n_groups = G ? d_in / G : 1;
+  const int n_groups = G ? d_in / G : (kStatic ? d_in / gsz : 1);
   float* sc = scales + static_cast<int64_t>(e) * n_groups * d_out;
   uint8_t* zr = zeros + static_cast<int64_t>(e) * n_groups * d_out;
   float s = 1.0f, z = 0.0f, inv_s = 1.0f;
-  if constexpr (G == 0) {
+  // static groups: the grid of each of this lane's columns (scale, 1 / scale, zero)
+  constexpr int CS = kStatic ? C : 1;
+  float g_s[CS], g_is[CS], g_z[CS];
+  if constexpr (kStatic) {
+    const int32_t* pe = perm + static_cast<int64_t>(e) * d_in + j0;
+#pragma unroll
+    for (int m = 0; m < C; ++m) {
+      const int c = min(max(pe[LPR * m + k], 0), d_in - 1);
+      const int64_t o = static_cast<int64_t>(c / gsz) * d_out + r;
+      g_s[m] = sc[o];
+      g_z[m] = static_cast<float>(zr[o]);
+      g_is[m] = 1.0f / g_s[m];
+    }
+  } else if constexpr (G == 0) {
     s = sc[r];
     z = static_cast<float>(zr[r]);
     inv_s = 1.0f / s;
@@ -297,14 +362,18 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
       }
       lo = grp_min<LPR>(lo);
       hi = grp_max<LPR>(hi);
-      s = fmaxf((hi - lo) / maxq, 1e-8f);
-      z = rintf(-lo / s);
+      fit_grid(lo, hi, maxq, sym != 0, s, z);
       inv_s = 1.0f / s;
       if (k == 0) {
         const int gi = (j0 + j) / G;
         sc[static_cast<int64_t>(gi) * d_out + r] = s;
         zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
       }
+    }
+    if constexpr (kStatic) {
+      s = grp_bcast<LPR, j % LPR>(g_s[mj]);
+      inv_s = grp_bcast<LPR, j % LPR>(g_is[mj]);
+      z = grp_bcast<LPR, j % LPR>(g_z[mj]);
     }
     const float wj = grp_bcast<LPR, j % LPR>(w[mj]);
     const float q = fminf(fmaxf(rintf(wj * inv_s) + z, 0.0f), maxq);
@@ -334,10 +403,12 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
 // codes[:, c] = codes_p[:, inv[c]]; g_idx[c] = inv[c] / group.  Staged like the weight
 // permute: inv once per workgroup, each codes_p row in LDS, 16 codes per thread per store.
 // kVec: the codes rows are 16-byte aligned.
+// by_orig (static groups): g_idx[c] = c / group.
 template <int DMAX, bool kVec>
 __global__ __launch_bounds__(256) void unpermute_staged_kernel(const uint8_t* __restrict__ codes_p,
                                                                const int32_t* __restrict__ inv, int d_out,
-                                                               int d_in, int group, uint8_t* __restrict__ codes,
+                                                               int d_in, int group, int by_orig,
+                                                               uint8_t* __restrict__ codes,
                                                                int32_t* __restrict__ g_idx) {
   __shared__ __attribute__((aligned(16))) uint8_t srow[DMAX];
   __shared__ uint16_t sidx[DMAX];
@@ -345,7 +416,7 @@ __global__ __launch_bounds__(256) void unpermute_staged_kernel(const uint8_t* __
   for (int c = t; c < d_in; c += 256) {
     const int j = min(max(inv[static_cast<int64_t>(e) * d_in + c], 0), d_in - 1);
     sidx[c] = static_cast<uint16_t>(j);
-    if (blockIdx.x == 0) g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? j / group : 0;
+    if (blockIdx.x == 0) g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? (by_orig ? c : j) / group : 0;
   }
   for (int i = 0; i < STAGE_ROWS; ++i) {
     const int r = blockIdx.x * STAGE_ROWS + i;
@@ -375,7 +446,7 @@ __global__ __launch_bounds__(256) void unpermute_staged_kernel(const uint8_t* __
 // One element per thread, for d_in beyond the largest staged row.
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ codes_p,
                                                         const int32_t* __restrict__ inv, int d_out, int d_in,
-                                                        int group, uint8_t* __restrict__ codes,
+                                                        int group, int by_orig, uint8_t* __restrict__ codes,
                                                         int32_t* __restrict__ g_idx) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   const int r = blockIdx.y;
@@ -384,7 +455,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restric
   const int j = min(max(inv[static_cast<int64_t>(e) * d_in + c], 0), d_in - 1);
   const int64_t ro = (static_cast<int64_t>(e) * d_out + r) * d_in;
   codes[ro + c] = codes_p[ro + j];
-  if (r == 0) g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? j / group : 0;
+  if (r == 0) g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? (by_orig ? c : j) / group : 0;
 }
 
 struct QuantWs {
@@ -419,8 +490,9 @@ struct SweepShape {
 // 512 threads for groups of 64 at 4 lanes per row, whose registers would not fit 1024).  The small
 // groups (16, 32) keep 16 lanes and 256 threads: their sweeps need too many registers
 // for more than one wave per SIMD.
-SweepShape sweep_shape(int G, int batch, int d_out) {
-  const bool wide_ok = G == 0 || G == 64 || G == 128;
+SweepShape sweep_shape(int G, bool stat, int batch, int d_out) {
+  // static groups keep 16 lanes per row: each lane also holds the grids of its columns
+  const bool wide_ok = !stat && (G == 0 || G == 64 || G == 128);
   const int64_t rows = static_cast<int64_t>(batch) * d_out;
   const int lpr = (wide_ok && rows / 16 >= 768) ? 4 : 16;
   int nt = 256;
@@ -438,24 +510,38 @@ SweepShape sweep_shape(int G, int batch, int d_out) {
   return {nt, lpr, dim3((d_out + rpw - 1) / rpw, batch)};
 }
 
-template <int G, int NT, int LPR>
-gptq_status launch_sweep(dim3 grid, hipStream_t stream, const float* Wp, const float* U, int64_t bsu, int d_out,
-                         int d_in, int blk, float maxq, float* scales, uint8_t* zeros, uint8_t* codes_p,
-                         float* err) {
-  GPTQ_LAUNCH((block_sweep_kernel<G, NT, LPR>), grid, dim3(NT), 0, stream, Wp, U, bsu, d_out, d_in, blk, maxq,
-              scales, zeros, codes_p, err);
+// Arguments of every sweep launch of one quantize call.
+struct SweepArgs {
+  const float* Wp;
+  const float* U;
+  int64_t bsu;
+  int d_out, d_in;
+  float maxq;
+  int sym;
+  const int32_t* perm;   // static groups: processing position -> original column
+  int gsz;               // static groups: group size
+  float* scales;
+  uint8_t* zeros;
+  uint8_t* codes_p;
+  float* err;
+};
+
+template <int G, int NT, int LPR, bool kStatic>
+gptq_status launch_sweep(dim3 grid, hipStream_t stream, const SweepArgs& a, int blk) {
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  timing_pair(GPTQ_TIME_SWEEP, &ev0, &ev1);
+  if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
+  GPTQ_LAUNCH((block_sweep_kernel<G, NT, LPR, kStatic>), grid, dim3(NT), 0, stream, a.Wp, a.U, a.bsu, a.d_out, a.d_in,
+              blk, a.maxq, a.sym, a.perm, a.gsz, a.scales, a.zeros, a.codes_p, a.err);
+  if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
   return GPTQ_OK;
 }
 
 template <int G>
-gptq_status launch_sweep_nt(const SweepShape& sh, hipStream_t stream, const float* Wp, const float* U, int64_t bsu,
-                            int d_out, int d_in, int blk, float maxq, float* scales, uint8_t* zeros,
-                            uint8_t* codes_p, float* err) {
+gptq_status launch_sweep_nt(const SweepShape& sh, hipStream_t stream, const SweepArgs& a, int blk) {
   if constexpr (G == 0 || G == 64 || G == 128) {
-#define GPTQ_SWEEP(NT, LPR)                                                                                    \
-  if (sh.nt == NT && sh.lpr == LPR)                                                                           \
-    return launch_sweep<G, NT, LPR>(sh.grid, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales, zeros, codes_p, \
-                                    err);
+#define GPTQ_SWEEP(NT, LPR) \
+  if (sh.nt == NT && sh.lpr == LPR) return launch_sweep<G, NT, LPR, false>(sh.grid, stream, a, blk);
     GPTQ_SWEEP(512, 16)   // 1024 threads at 16 lanes: never chosen (4 lanes take over first)
     if constexpr (G != 64) {
       GPTQ_SWEEP(1024, 4)
@@ -465,21 +551,20 @@ gptq_status launch_sweep_nt(const SweepShape& sh, hipStream_t stream, const floa
 #undef GPTQ_SWEEP
   }
   if (sh.nt != 256 || sh.lpr != 16) return GPTQ_ERR_UNSUPPORTED;
-  return launch_sweep<G, 256, 16>(sh.grid, stream, Wp, U, bsu, d_out, d_in, blk, maxq, scales, zeros, codes_p, err);
+  return launch_sweep<G, 256, 16, false>(sh.grid, stream, a, blk);
 }
 
-gptq_status sweep_block(int b, int G, const SweepShape& sg, hipStream_t stream, int d_out, int d_in,
-                        const QuantWs& w, const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
+gptq_status sweep_block(int b, int G, bool stat, const SweepShape& sg, hipStream_t stream, const SweepArgs& a) {
+  if (stat) {
+    if (sg.nt != 256 || sg.lpr != 16) return GPTQ_ERR_UNSUPPORTED;
+    return launch_sweep<0, 256, 16, true>(sg.grid, stream, a, b);
+  }
   switch (G) {
-    case 0: return launch_sweep_nt<0>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 16:
-      return launch_sweep_nt<16>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 32:
-      return launch_sweep_nt<32>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 64:
-      return launch_sweep_nt<64>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
-    case 128:
-      return launch_sweep_nt<128>(sg, stream, w.Wp, U, bsu, d_out, d_in, b, maxq, scales, zeros, w.codes_p, w.err);
+    case 0: return launch_sweep_nt<0>(sg, stream, a, b);
+    case 16: return launch_sweep_nt<16>(sg, stream, a, b);
+    case 32: return launch_sweep_nt<32>(sg, stream, a, b);
+    case 64: return launch_sweep_nt<64>(sg, stream, a, b);
+    case 128: return launch_sweep_nt<128>(sg, stream, a, b);
     default: return GPTQ_ERR_UNSUPPORTED;
   }
 }
@@ -491,20 +576,26 @@ gptq_status sweep_block(int b, int G, const SweepShape& sg, hipStream_t stream, 
 // split, after j's error is known and before k is quantized, so the updates are the same
 // as applying each block's errors to all later columns right after the block; only the
 // time at which they land changes.  Most of the flops move into a few large products.
-gptq_status sweep_range(int b0, int b1, int G, const SweepShape& sg, hipStream_t stream, int batch, int d_out, int d_in,
-                        const QuantWs& w, const float* U, int64_t bsu, float maxq, float* scales, uint8_t* zeros) {
-  if (b1 - b0 == 1) return sweep_block(b0, G, sg, stream, d_out, d_in, w, U, bsu, maxq, scales, zeros);
+gptq_status sweep_range(int b0, int b1, int G, bool stat, const SweepShape& sg, hipStream_t stream, int batch,
+                        const SweepArgs& a) {
+  if (b1 - b0 == 1) return sweep_block(b0, G, stat, sg, stream, a);
   const int bm = b0 + (b1 - b0) / 2;
-  gptq_status st = sweep_range(b0, bm, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales, zeros);
+  gptq_status st = sweep_range(b0, bm, G, stat, sg, stream, batch, a);
   if (st != GPTQ_OK) return st;
+  const int d_in = a.d_in;
   GemmArgs g{};
-  g.M = d_out; g.N = (b1 - bm) * kBlock; g.K = (bm - b0) * kBlock;
-  g.A = w.err + static_cast<int64_t>(b0) * kBlock; g.lda = d_in; g.sA = static_cast<int64_t>(d_out) * d_in;
-  g.B = U + static_cast<int64_t>(b0) * kBlock * d_in + static_cast<int64_t>(bm) * kBlock; g.ldb = d_in; g.sB = bsu;
-  g.C = w.Wp + static_cast<int64_t>(bm) * kBlock; g.ldc = d_in; g.sC = static_cast<int64_t>(d_out) * d_in;
-  g.alpha = -1.0f; g.beta = 1.0f; g.transB = 0; g.flags = 0; g.batch = batch;
+  g.M = a.d_out; g.N = (b1 - bm) * kBlock; g.K = (bm - b0) * kBlock;
+  g.A = a.err + static_cast<int64_t>(b0) * kBlock; g.lda = d_in; g.sA = static_cast<int64_t>(a.d_out) * d_in;
+  g.B = a.U + static_cast<int64_t>(b0) * kBlock * d_in + static_cast<int64_t>(bm) * kBlock; g.ldb = d_in; g.sB = a.bsu;
+  g.C = const_cast<float*>(a.Wp) + static_cast<int64_t>(bm) * kBlock; g.ldc = d_in;
+  g.sC = static_cast<int64_t>(a.d_out) * d_in;
+  g.alpha = -1.0f; g.beta = 1.0f; g.transB = 0; g.flags = 0; g.batch = batch; g.role = 1;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  timing_pair(GPTQ_TIME_LAZY_GEMM, &ev0, &ev1);
+  if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
   if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
-  return sweep_range(bm, b1, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales, zeros);
+  if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
+  return sweep_range(bm, b1, G, stat, sg, stream, batch, a);
 }
 
 }  // namespace
@@ -572,27 +663,44 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
     if (st != GPTQ_OK) return st;
   }
   GPTQ_LAUNCH(inverse_perm_kernel, dim3(cb, batch), blk, 0, stream, perm, d_in, w.inv);
+  const bool stat = p.static_groups != 0 && G > 0;
   if (G == 0) {
-    GPTQ_LAUNCH(row_grid_kernel, dim3(d_out, batch), blk, 0, stream, w.Wp, d_out, d_in, maxq, scales, zeros);
+    GPTQ_LAUNCH(row_grid_kernel, dim3(d_out, batch), blk, 0, stream, w.Wp, d_out, d_in, maxq, p.sym, scales, zeros);
+  } else if (stat) {
+    const dim3 gg(static_cast<unsigned>((static_cast<int64_t>(d_in / G) * d_out + 255) / 256), batch);
+    switch (w_dtype) {
+      case GPTQ_F32:
+        GPTQ_LAUNCH(static_grid_kernel<float>, gg, blk, 0, stream, static_cast<const float*>(W), ldw, bsw, dead, d_out,
+                    d_in, G, maxq, p.sym, scales, zeros);
+        break;
+      case GPTQ_BF16:
+        GPTQ_LAUNCH(static_grid_kernel<BF16>, gg, blk, 0, stream, static_cast<const BF16*>(W), ldw, bsw, dead, d_out,
+                    d_in, G, maxq, p.sym, scales, zeros);
+        break;
+      case GPTQ_F16:
+        GPTQ_LAUNCH(static_grid_kernel<F16>, gg, blk, 0, stream, static_cast<const F16*>(W), ldw, bsw, dead, d_out,
+                    d_in, G, maxq, p.sym, scales, zeros);
+        break;
+    }
   }
-  const SweepShape sg = sweep_shape(G, batch, d_out);
-  const gptq_status st = sweep_range(0, d_in / kBlock, G, sg, stream, batch, d_out, d_in, w, U, bsu, maxq, scales,
-                                     zeros);
+  const SweepShape sg = sweep_shape(G, stat, batch, d_out);
+  const SweepArgs sa{w.Wp, U, bsu, d_out, d_in, maxq, p.sym, perm, G, scales, zeros, w.codes_p, w.err};
+  const gptq_status st = sweep_range(0, d_in / kBlock, stat ? 0 : G, stat, sg, stream, batch, sa);
   if (st != GPTQ_OK) return st;
   {
     const bool vec = reinterpret_cast<uintptr_t>(codes) % 16 == 0;
     auto staged = [&](auto dmax) {
       constexpr int DM = decltype(dmax)::value;
       if (vec) GPTQ_LAUNCH((unpermute_staged_kernel<DM, true>), sgr, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G,
-                           codes, g_idx);
+                           int(stat), codes, g_idx);
       else GPTQ_LAUNCH((unpermute_staged_kernel<DM, false>), sgr, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G,
-                       codes, g_idx);
+                       int(stat), codes, g_idx);
       return GPTQ_OK;
     };
     gptq_status st = GPTQ_OK;
     if (d_in <= 4096) st = staged(std::integral_constant<int, 4096>{});
     else if (d_in <= kStagedMax) st = staged(std::integral_constant<int, kStagedMax>{});
-    else GPTQ_LAUNCH(unpermute_kernel, pg, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G, codes, g_idx);
+    else GPTQ_LAUNCH(unpermute_kernel, pg, blk, 0, stream, w.codes_p, w.inv, d_out, d_in, G, int(stat), codes, g_idx);
     if (st != GPTQ_OK) return st;
   }
   return GPTQ_OK;

@@ -40,21 +40,26 @@ class NotSPDError(GptqError):
 
 class _Params(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int), ("group_size", ctypes.c_int), ("block_size", ctypes.c_int),
-                ("damp", ctypes.c_float), ("act_order", ctypes.c_int)]
+                ("damp", ctypes.c_float), ("act_order", ctypes.c_int), ("sym", ctypes.c_int),
+                ("static_groups", ctypes.c_int)]
 
 
 @dataclasses.dataclass(frozen=True)
 class Params:
-    """Quantizer knobs: bits, group_size (-1 = per row), block_size (128), damp, act_order."""
+    """Quantizer knobs: bits, group_size (-1 = per row), block_size (128), damp, act_order,
+    sym (symmetric grid), static_groups (groups of original columns fitted up front)."""
 
     bits: int = 4
     group_size: int = 128
     block_size: int = 128
     damp: float = 0.01
     act_order: bool = False
+    sym: bool = False
+    static_groups: bool = False
 
     def c(self) -> _Params:
-        return _Params(self.bits, self.group_size, self.block_size, self.damp, int(self.act_order))
+        return _Params(self.bits, self.group_size, self.block_size, self.damp, int(self.act_order), int(self.sym),
+                       int(self.static_groups))
 
     def n_groups(self, d_in: int) -> int:
         return 1 if self.group_size == -1 else d_in // self.group_size
@@ -85,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.gptq_version.argtypes = []
     L.gptq_version.restype = ctypes.c_char_p
     L.gptq_timing_enable.argtypes = [i32]
-    L.gptq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.gptq_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_int4",
                  "gptq_timing_enable", "gptq_timing_read"):
         getattr(L, name).restype = i32
@@ -112,6 +117,16 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _keep_for(stream, *tensors) -> None:
+    """Tensors this module allocated (on torch's current stream) and hands to kernels on
+    another stream: tell the caching allocator about that stream, so that their memory
+    is not given to new work before the kernels queued there are done with it."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        t.record_stream(stream)
+
+
 def _batched(t: torch.Tensor, nd: int) -> torch.Tensor:
     return t.unsqueeze(0) if t.dim() == nd else t
 
@@ -122,10 +137,12 @@ def workspace_size(which: int, batch: int, d_out: int, d_in: int, n_tokens_hint:
     return int(lib().gptq_workspace_size(which, batch, d_out, d_in, n_tokens_hint, ctypes.byref(p)))
 
 
-def _workspace(nbytes: int, device, workspace: torch.Tensor | None) -> torch.Tensor:
+def _workspace(nbytes: int, device, workspace: torch.Tensor | None, stream=None) -> torch.Tensor:
     if workspace is not None and workspace.numel() >= nbytes:
         return workspace
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _keep_for(stream, ws)
+    return ws
 
 
 def new_hessian(d_in: int, batch: int | None = None, device="cuda"):
@@ -148,7 +165,7 @@ def accumulate_hessian(X: torch.Tensor, H: torch.Tensor, diag_key: torch.Tensor,
         raise ValueError("shape mismatch between X, H, diag_key, n_seen")
     if Xb.stride(2) != 1 or not Hb.is_contiguous() or not diag_key.is_contiguous():
         raise ValueError("X rows must be contiguous; H and diag_key contiguous")
-    ws = _workspace(workspace_size(WS_HESSIAN, batch, 0, d_in, n), X.device, workspace)
+    ws = _workspace(workspace_size(WS_HESSIAN, batch, 0, d_in, n), X.device, workspace, stream)
     _check(lib().gptq_accumulate_hessian(batch, d_in, n, _DT[X.dtype], Xb.data_ptr(), Xb.stride(1),
                                          Xb.stride(0) if batch > 1 else n * Xb.stride(1), Hb.data_ptr(),
                                          d_in * d_in, diag_key.data_ptr(), n_seen.data_ptr(), ws.data_ptr(),
@@ -167,7 +184,8 @@ def prepare_hinv(H: torch.Tensor, diag_key: torch.Tensor, params: Params, worksp
     U = torch.empty(*H.shape, dtype=torch.float32, device=H.device)
     perm = torch.empty(*shp, dtype=torch.int32, device=H.device)
     dead = torch.empty(*shp, dtype=torch.uint8, device=H.device)
-    ws = _workspace(workspace_size(WS_PREPARE, batch, 0, d_in, 0, params), H.device, workspace)
+    _keep_for(stream, U, perm, dead)
+    ws = _workspace(workspace_size(WS_PREPARE, batch, 0, d_in, 0, params), H.device, workspace, stream)
     p = params.c()
     _check(lib().gptq_prepare_hinv(batch, d_in, Hb.data_ptr(), d_in * d_in, diag_key.data_ptr(), ctypes.byref(p),
                                    U.data_ptr(), d_in * d_in, perm.data_ptr(), dead.data_ptr(), ws.data_ptr(),
@@ -191,7 +209,8 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
     scales = torch.empty(*lead, ng, d_out, dtype=torch.float32, device=W.device)
     zeros = torch.empty(*lead, ng, d_out, dtype=torch.uint8, device=W.device)
     g_idx = torch.empty(*lead, d_in, dtype=torch.int32, device=W.device)
-    ws = _workspace(workspace_size(WS_QUANTIZE, batch, d_out, d_in, 0, params), W.device, workspace)
+    _keep_for(stream, codes, scales, zeros, g_idx)
+    ws = _workspace(workspace_size(WS_QUANTIZE, batch, d_out, d_in, 0, params), W.device, workspace, stream)
     p = params.c()
     _check(lib().gptq_quantize_layer(batch, d_out, d_in, _DT[W.dtype], Wb.data_ptr(), Wb.stride(1),
                                      Wb.stride(0) if batch > 1 else d_out * Wb.stride(1), U.data_ptr(),
@@ -213,21 +232,26 @@ def pack_int4(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, st
     qweight = torch.empty(*lead, d_in // 8, d_out, dtype=torch.int32, device=codes.device)
     qzeros = torch.empty(*lead, ng, d_out // 8, dtype=torch.int32, device=codes.device)
     sf16 = torch.empty(*lead, ng, d_out, dtype=torch.float16, device=codes.device)
+    _keep_for(stream, qweight, qzeros, sf16)
     _check(lib().gptq_pack_int4(batch, d_out, d_in, ng, codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
                                 qweight.data_ptr(), qzeros.data_ptr(), sf16.data_ptr(), _stream(stream)),
            "gptq_pack_int4")
     return qweight, qzeros, sf16
 
 
+TIME_SYRK, TIME_LAZY_GEMM, TIME_SWEEP, TIME_PACK = 0, 1, 2, 3
+
+
 def timing_enable(on: bool = True) -> None:
-    """Start/stop recording HIP events around every Hessian SYRK kernel launch."""
+    """Start/stop recording HIP events around every timed kernel launch (SYRK, lazy-update
+    products, column sweeps, packing)."""
     _check(lib().gptq_timing_enable(int(on)), "gptq_timing_enable")
 
 
-def timing_read():
-    """(summed SYRK kernel milliseconds, launches) since the previous read."""
+def timing_read(which: int = TIME_SYRK):
+    """(summed kernel milliseconds, launches) of one timed class since its previous read."""
     ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
-    _check(lib().gptq_timing_read(ctypes.byref(ms), ctypes.byref(n)), "gptq_timing_read")
+    _check(lib().gptq_timing_read(which, ctypes.byref(ms), ctypes.byref(n)), "gptq_timing_read")
     return ms.value, n.value
 
 

@@ -10,7 +10,8 @@ sections "Groups, act-order and other knobs" and "Worked example: a 7B model") a
 stood in for by random activations with the same shapes and the value structure
 below; no dataset item is used or reproduced.
 
-* ``W``: i.i.d. N(0, sigma^2), stored as fp32 or bf16 (RNE from fp32).
+* ``W``: i.i.d. N(0, sigma^2), stored as fp32, bf16 or fp16 (round to nearest even
+  from fp32).
 * ``lognormal`` activations: x[t, c] = N(0, 1) * s_c with s_c = exp(N(0, 1)), so the
   Hessian diagonal spans several decades; optionally a fraction of "outlier"
   channels (chosen without replacement) get s_c multiplied by a factor.
@@ -31,7 +32,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = [
-    "LayerSpec", "CONFIGS", "config", "scaled", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "LayerSpec", "CONFIGS", "config", "scaled", "f32_to_bf16_bits", "bf16_bits_to_f32", "f32_to_f16_bits",
     "make_weight", "make_channel_scales", "make_sequence", "make_activations",
 ]
 
@@ -45,7 +46,7 @@ class LayerSpec:
     d_in: int
     n_tokens: int              # calibration tokens per layer
     seq_len: int = 2048        # tokens per generated sequence (one RNG stream each)
-    dtype: str = "bf16"        # storage dtype of W and X: "bf16" or "f32"
+    dtype: str = "bf16"        # storage dtype of W and X: "bf16", "f16" or "f32"
     w_sigma: float = 0.02
     x_kind: str = "lognormal"  # "lognormal" or "relu2"
     outlier_frac: float = 0.0  # fraction of outlier channels (lognormal only)
@@ -56,6 +57,8 @@ class LayerSpec:
     block_size: int = 128
     damp: float = 0.01
     act_order: bool = True
+    sym: bool = False          # symmetric grid (zero point at the middle level)
+    static_groups: bool = False  # groups of consecutive original columns, fitted up front
     batch: int = 1             # independent experts, each with its own seed
     seed: int = 0
 
@@ -109,16 +112,23 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to fp16 (round-to-nearest-even, numpy's cast) and return the 16-bit patterns."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return f32_to_bf16_bits(a32)
+    if dtype == "f16":
+        return f32_to_f16_bits(a32)
     if dtype == "f32":
         return np.ascontiguousarray(a32, dtype=np.float32)
     raise ValueError(dtype)
 
 
 def make_weight(spec: LayerSpec, e: int = 0) -> np.ndarray:
-    """W [d_out, d_in] as fp32 or bf16 bit patterns (uint16)."""
+    """W [d_out, d_in] as fp32, or bf16 / fp16 bit patterns (uint16)."""
     rng = np.random.default_rng([spec.layer_seed(e), 0])
     w = rng.standard_normal((spec.d_out, spec.d_in), dtype=np.float32) * np.float32(spec.w_sigma)
     return _store(w, spec.dtype)
@@ -161,7 +171,7 @@ def make_sequence(spec: LayerSpec, s: int, length: int, scales: np.ndarray | Non
 def make_activations(spec: LayerSpec, e: int = 0, out: np.ndarray | None = None,
                      threads: int | None = None) -> np.ndarray:
     """All calibration tokens of layer ``e`` as one token-major array [n_tokens, d_in]."""
-    dt = np.uint16 if spec.dtype == "bf16" else np.float32
+    dt = np.uint16 if spec.dtype in ("bf16", "f16") else np.float32
     if out is None:
         out = np.empty((spec.n_tokens, spec.d_in), dtype=dt)
     scales = make_channel_scales(spec, e)

@@ -31,9 +31,14 @@ def test_library_exports_every_declared_symbol():
 
 def test_timing_hook_without_launches():
     gptq.timing_enable(True)
-    assert gptq.timing_read() == (0.0, 0)
+    for k in (gptq.TIME_SYRK, gptq.TIME_LAZY_GEMM, gptq.TIME_SWEEP, gptq.TIME_PACK):
+        assert gptq.timing_read(k) == (0.0, 0)
     gptq.timing_enable(False)
-    assert gptq.lib().gptq_timing_read(None, None) == gptq.GPTQ_ERR_INVALID_ARG
+    L = gptq.lib()
+    assert L.gptq_timing_read(0, None, None) == gptq.GPTQ_ERR_INVALID_ARG
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert L.gptq_timing_read(4, ctypes.byref(ms), ctypes.byref(n)) == gptq.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == gptq.GPTQ_ERR_INVALID_ARG
 
 
 def test_status_strings():

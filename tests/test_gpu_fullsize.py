@@ -6,10 +6,12 @@ attn_proj, mlp_up and the MoE experts: the full fp64 oracle (H, U) and a teacher
 replay of sampled rows (rows are independent given U) under the rules of tests/parity.py.
 
 mlp_down (d_in 14336, 262144 tokens): its fp64 Hessian takes ~1e14 flops on the host, so
-by default it gets the checks the oracle can make without it: sampled blocks of H (the
-relative Frobenius error estimated from them), every channel energy, dead inputs and the
-ActOrder permutation, g_idx, code range, U's structure, and the int4 packing round trip.
-With GPTQ_FULL_ORACLE=1 the full oracle comparison of the other layers runs as well.
+H is pinned on sampled blocks (the relative Frobenius error estimated from them) and on
+every fp64 channel energy; the oracle then factors the Hessian made of the GPU's
+off-diagonal entries (pinned by the blocks) and its own fp64 diagonal, and the rules of
+tests/parity.py apply from there on: dead inputs, the ActOrder permutation, U, the
+teacher-forced replay of sampled rows, scales, g_idx and the layer loss.  With
+GPTQ_FULL_ORACLE=1 the oracle accumulates the full fp64 Hessian from X instead.
 """
 import os
 
@@ -75,7 +77,9 @@ def test_full_size_mlp_down():
     spec = synth.config("mlp_down")
     announce(f"full size {spec}")
     Ws, Xs = parity.make_inputs(spec)
+    parity._progress("inputs ready; GPU layer")
     g = parity.run_gpu(spec, Ws, Xs)
+    parity._progress("GPU layer done; sampled Hessian blocks")
     X, d = Xs[0], spec.d_in
     assert int(g["n_seen"].reshape(-1)[0]) == spec.n_tokens
     Hg = g["H"][0]
@@ -93,25 +97,19 @@ def test_full_size_mlp_down():
         den += float(np.sum(Bref ** 2))
     h_rel = (num / den) ** 0.5
     assert h_rel <= parity.TOL_H, h_rel
-    # every channel energy (fp64), dead inputs, ActOrder permutation, g_idx
+    # every channel energy (fp64)
+    parity._progress("channel energies")
     key = R.ref_channel_energy(X, spec.dtype)
     key_rel = float(np.max(np.abs(g["diag_key"][0] - key) / np.maximum(np.abs(key), 1e-300)))
     assert key_rel <= parity.TOL_KEY, key_rel
-    perm, dead, _ = R.ref_column_order(key, spec.act_order)
-    assert np.array_equal(g["dead"][0].astype(bool), dead)
-    assert np.array_equal(g["perm"][0].astype(np.int64), perm)
-    inv = np.empty_like(perm)
-    inv[perm] = np.arange(d)
-    assert np.array_equal(g["g_idx"][0], (inv // spec.group_size).astype(np.int32))
-    # U: upper triangular with a positive finite diagonal; codes on the grid
-    U = g["U"][0]
-    assert np.all(np.tril(U, -1) == 0)
-    du = np.diag(U)
-    assert np.all(np.isfinite(du)) and np.all(du > 0)
-    assert int(g["codes"][0].max()) <= (1 << spec.bits) - 1
-    assert np.all(np.isfinite(g["scales"][0])) and np.all(g["scales"][0] > 0)
-    check_pack(g, 0)
     print("mlp_down", dict(H_rel_fro_sampled=h_rel, key_rel=key_rel), flush=True)
+    check_pack(g, 0)
+    rows = sample_rows(spec.d_out, 30, seed=31)
     if os.environ.get("GPTQ_FULL_ORACLE") == "1":
-        rep = parity.check_problem(spec, Ws[0], X, g, 0, rows=sample_rows(spec.d_out, 30, seed=31))
-        print("mlp_down full oracle", short(rep), flush=True)
+        rep = parity.check_problem(spec, Ws[0], X, g, 0, rows=rows)
+    else:
+        H = Hg.astype(np.float64)
+        H[np.diag_indices(d)] = key
+        del g["H"]
+        rep = parity.check_problem(spec, Ws[0], X, g, 0, rows=rows, H=H)
+    print("mlp_down oracle", short(rep), flush=True)

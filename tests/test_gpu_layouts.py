@@ -208,3 +208,30 @@ def test_wide_input_quantize_diagonal():
                 n_div += 1
     print("divergences at midpoints:", n_div, "of", got.size, flush=True)
     assert n_div <= parity.TOL_DIV_FRAC * got.size
+
+
+def test_calls_on_a_non_current_stream():
+    # every call enqueued on a side stream while torch's current stream stays the default
+    # one: the binding's own allocations are kept alive for that stream, and the results
+    # equal those of the same calls on the current stream bit for bit
+    spec = synth.scaled("attn_proj", d_out=96, d_in=384, n_tokens=2500, seq_len=500)
+    announce("all four calls on a non-current stream")
+    import torch
+    from post_weight_quantization_03_amd import gptq
+    Ws, Xs = parity.make_inputs(spec)
+    p = parity.params_of(spec)
+    W = parity.to_torch(Ws[0], spec.dtype)
+    X = parity.to_torch(Xs[0], spec.dtype)
+    ref = parity.run_gpu(spec, Ws, Xs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    H, key, n = gptq.new_hessian(spec.d_in)
+    side.wait_stream(torch.cuda.current_stream())
+    gptq.accumulate_hessian(X, H, key, n, stream=side)
+    U, perm, dead = gptq.prepare_hinv(H, key, p, stream=side)
+    codes, scales, zeros, g_idx = gptq.quantize_layer(W, U, perm, dead, p, stream=side)
+    qw, qz, sf = gptq.pack_int4(codes, scales, zeros, stream=side)
+    side.synchronize()
+    got = dict(H=H, U=U, perm=perm, codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, qweight=qw)
+    for k, v in got.items():
+        assert np.array_equal(v.cpu().numpy(), ref[k][0]), k

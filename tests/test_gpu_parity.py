@@ -5,6 +5,7 @@ tiles and ragged tails (d_out not a multiple of 64, token counts not a multiple 
 32-token stage, d_in not a multiple of the 256-wide Hessian tile).  Acceptance rules are
 in tests/parity.py.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -47,6 +48,25 @@ CASES = {
     "per_row_4_lanes": synth.scaled("moe", d_out=520, d_in=256, n_tokens=600, batch=24, seq_len=300,
                                     group_size=-1),
     "group128_4_lanes_512": synth.scaled("moe", d_out=512, d_in=128, n_tokens=400, batch=64, seq_len=200),
+    # fp16 inputs (the f16 matrix-core SYRK, fp16 channel energies and weight permutes)
+    "fp16_attn_scaled": synth.scaled("attn_proj", d_out=136, d_in=384, n_tokens=3000, seq_len=1000, dtype="f16"),
+    "fp16_moe_scaled": synth.scaled("moe", d_out=64, d_in=256, n_tokens=900, batch=3, seq_len=300, dtype="f16",
+                                    bits=3),
+    # symmetric grids and static groups ("GPTQ Architecture, in depth", "Groups, act-order and
+    # other knobs"), across per-row, every group size and both lane layouts of the sweep
+    "sym_g128_actorder": synth.scaled("attn_proj", d_out=200, d_in=512, n_tokens=5000, seq_len=1024, sym=True),
+    "sym_per_row_many_rows": synth.scaled("moe", d_out=520, d_in=256, n_tokens=600, batch=16, seq_len=300,
+                                          group_size=-1, sym=True),
+    "sym_g32_3bit": synth.scaled("mlp_down", d_out=72, d_in=256, n_tokens=1500, seq_len=500, group_size=32, bits=3,
+                                 sym=True),
+    "static_g128_actorder": synth.scaled("attn_proj", d_out=136, d_in=512, n_tokens=4000, seq_len=1000,
+                                         static_groups=True),
+    "static_g16_sym_f32": synth.scaled("attn_proj", d_out=40, d_in=384, n_tokens=1500, seq_len=500, group_size=16,
+                                       dtype="f32", sym=True, static_groups=True),
+    "static_g64_moe_many_rows": synth.scaled("moe", d_out=512, d_in=256, n_tokens=600, batch=8, seq_len=300,
+                                             group_size=64, static_groups=True),
+    "static_no_actorder": synth.scaled("mlp_up", d_out=96, d_in=256, n_tokens=1200, seq_len=600,
+                                       static_groups=True),
     # 36 block columns: the Cholesky's far updates grouped four panels at a time; lazy updates,
     # trailing updates and the triangular inverse large enough for the split-bf16 products
     # (ragged row tiles: 1944 = 15 x 128 + 24; both B layouts; lower-only output)
@@ -63,6 +83,40 @@ def test_layer_parity(name):
     for e in range(spec.batch):
         rep = parity.check_problem(spec, Ws[e], Xs[e], g, e)
         print(name, e, {k: (round(v, 9) if isinstance(v, float) else v) for k, v in rep.items()}, flush=True)
+
+
+def test_exact_rounding_ties_match_exactly():
+    # One-hot calibration tokens give a diagonal H, so nothing is propagated and every code
+    # is the grid's own decision on the exact bf16 weight.  The rows are built so that
+    # w / scale lands exactly on a half integer with an odd zero point: the quotient is
+    # rounded (half to even) before the zero point is added ("GPTQ Architecture, in
+    # depth", "The algorithm in code"), which the oracle and the kernel must both do.
+    announce("exact rounding ties, diagonal H")
+    d_out, d_in = 16, 256
+    spec = synth.scaled("attn_proj", d_out=d_out, d_in=d_in, n_tokens=2 * d_in, seq_len=2 * d_in, act_order=False,
+                        group_size=-1)
+    rng = np.random.default_rng(5)
+    X = np.zeros((2 * d_in, d_in), dtype=np.float32)
+    X[np.arange(2 * d_in), np.arange(2 * d_in) % d_in] = 1.0 + rng.integers(0, 8, size=2 * d_in) / 8.0
+    halves = np.arange(-1, 14) + 0.5                     # -0.5 .. 13.5, each a tie under scale 1
+    W = rng.choice(halves, size=(d_out, d_in)).astype(np.float32)
+    # every group of 16 spans [-1, 14]: asymmetric scale 1 and zero 1, symmetric scale 2,
+    # both exact in fp32, so only the rounding rule decides the ties
+    W[:, 0::16], W[:, 1::16] = -1.0, 14.0
+    Xb, Wb = synth.f32_to_bf16_bits(X), synth.f32_to_bf16_bits(W)
+    assert np.array_equal(synth.bf16_bits_to_f32(Wb), W)
+    for group, sym in [(-1, False), (16, False), (-1, True)]:
+        sp = dataclasses.replace(spec, group_size=group, sym=sym)
+        g = parity.run_gpu(sp, [Wb], [Xb])
+        H, _ = R.ref_accumulate_hessian(Xb, "bf16")
+        prep = R.ref_prepare_hinv(H, sp.damp, sp.act_order)
+        ref = R.ref_quantize_layer(Wb, "bf16", prep, sp.bits, group, sym=sym)
+        assert np.array_equal(g["codes"][0], ref["codes"]), (group, sym)
+        assert np.array_equal(g["zeros"][0], ref["zeros"]), (group, sym)
+        n_ties = int(np.sum(np.abs(ref["grid"].pre - np.floor(ref["grid"].pre) - 0.5) == 0))
+        print("exact ties", group, sym, n_ties, flush=True)
+        if not sym:
+            assert n_ties > d_out * d_in // 4
 
 
 def test_chunked_accumulation_and_empty_chunk():
