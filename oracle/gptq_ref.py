@@ -68,7 +68,7 @@ __all__ = [
     "NotSPD", "widen", "ref_accumulate_hessian", "ref_channel_energy", "ref_hessian_entries",
     "ref_column_order", "ref_prepare_hinv", "UniformGrid", "obs_sweep", "GridDecisions",
     "ref_quantize_layer", "ref_dequantize", "ref_layer_loss", "ref_pack_int4", "ref_unpack_int4",
-    "ref_gptq_layer",
+    "ref_w4a16_matmul", "ref_gptq_layer",
 ]
 
 
@@ -438,6 +438,21 @@ def ref_unpack_int4(qweight: np.ndarray, qzeros: np.ndarray):
     for k in range(8):
         zeros[:, k::8] = (qz >> np.uint32(4 * k)) & np.uint32(15)
     return codes.T.copy(), zeros
+
+
+# ------------------------------------- serving: W4A16 product from the checkpoint tensors
+
+def ref_w4a16_matmul(X: np.ndarray, dtype: str, qweight: np.ndarray, qzeros: np.ndarray,
+                     scales_f16: np.ndarray, g_idx: np.ndarray) -> np.ndarray:
+    """Y = X What^T in fp64 from the packed checkpoint ([ARCH] "Packing, tooling and serving":
+    4-bit weights with 16-bit activations, dequantized right before the product; [LIN]
+    section 8 for the tensors).  X [m, d_in] (bf16 / fp16 bits, or fp32); the weights are
+    unpacked, each dequantized with its fp16 scale and zero of group g_idx[c], and the
+    product is taken in fp64.  Returns Y [m, d_out]."""
+    codes, zeros = ref_unpack_int4(qweight, qzeros)
+    scales = np.asarray(scales_f16, dtype=np.float16).astype(np.float64)
+    What = ref_dequantize(codes, scales, zeros, np.asarray(g_idx))
+    return widen(X, dtype) @ What.T
 
 
 # ------------------------------------------------------------------- whole layer
