@@ -48,7 +48,9 @@ typedef enum {
   GPTQ_ERR_NOT_SPD = -2,     /* the damped Hessian has no Cholesky factor                 */
   GPTQ_ERR_HIP = -3,         /* a HIP runtime call failed                                  */
   GPTQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than gptq_workspace_size()   */
-  GPTQ_ERR_UNSUPPORTED = -5  /* valid request outside what this build implements          */
+  GPTQ_ERR_UNSUPPORTED = -5, /* valid request outside what this build implements          */
+  GPTQ_ERR_TOO_LARGE = -6    /* problem exceeds the fixed scratch of the allocation-free
+                                entry point (gptq_quantize_layer_noalloc)                  */
 } gptq_status;
 
 typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
@@ -168,6 +170,30 @@ gptq_status gptq_quantize_layer(int batch, int d_out, int d_in, gptq_dtype w_dty
                                 const gptq_params* p, uint8_t* codes, float* scales,
                                 uint8_t* zeros, int32_t* g_idx, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Allocation-free variant of gptq_quantize_layer, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and kernels as gptq_quantize_layer, without the
+ * workspace: the call's scratch (per problem: fp32 working weights and errors, codes in
+ * processing order, 9 bytes per weight, plus the inverse permutation) lives in a fixed
+ * device array of GPTQ_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU,
+ * held until the process ends; the call itself allocates and frees nothing.  A problem
+ * that needs more (about 7.4 million weights over all problems of the batch) is rejected
+ * with GPTQ_ERR_TOO_LARGE before anything is enqueued.  The array's address is looked up
+ * once per device, on the first call there.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that overlap in time on one GPU
+ * (different streams, or different host threads) race; calls in order on one stream do
+ * not.  Nothing in the array needs to start at zero.  The timing hook does not bracket
+ * this variant's kernels.
+ */
+#define GPTQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gptq_status gptq_quantize_layer_noalloc(int batch, int d_out, int d_in, gptq_dtype w_dtype,
+                                        const void* W, int64_t ldw, int64_t batch_stride_w,
+                                        const float* U, int64_t batch_stride_u,
+                                        const int32_t* perm, const uint8_t* dead,
+                                        const gptq_params* p, uint8_t* codes, float* scales,
+                                        uint8_t* zeros, int32_t* g_idx, hipStream_t stream);
 
 /*
  * Checkpoint packing — "04 — GPTQ: ...", section 8, and "GPTQ Architecture, in

@@ -85,6 +85,13 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
                              uint8_t* zeros, int32_t* g_idx, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 size_t quantize_workspace(int batch, int d_out, int d_in, const gptq_params& p);
+// The same call with the library's fixed device scratch array instead of a workspace
+// (GPTQ_NOALLOC_SCRATCH_BYTES); GPTQ_ERR_TOO_LARGE when the problem needs more.
+constexpr size_t kNoAllocScratchBytes = GPTQ_NOALLOC_SCRATCH_BYTES;
+gptq_status quantize_noalloc_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W,
+                                     int64_t ldw, int64_t bsw, const float* U, int64_t bsu, const int32_t* perm,
+                                     const uint8_t* dead, const gptq_params& p, uint8_t* codes, float* scales,
+                                     uint8_t* zeros, int32_t* g_idx, hipStream_t stream);
 
 gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uint8_t* codes,
                          const float* scales, const uint8_t* zeros, int32_t* qweight, int32_t* qzeros,

@@ -158,11 +158,12 @@ gptq_status gptq_prepare_hinv(int batch, int d_in, const float* H, int64_t batch
   return not_spd ? GPTQ_ERR_NOT_SPD : GPTQ_OK;
 }
 
-gptq_status gptq_quantize_layer(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
-                                int64_t batch_stride_w, const float* U, int64_t batch_stride_u, const int32_t* perm,
-                                const uint8_t* dead, const gptq_params* p, uint8_t* codes, float* scales,
-                                uint8_t* zeros, int32_t* g_idx, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+namespace {
+// Arguments shared by gptq_quantize_layer and its allocation-free variant.
+gptq_status check_quantize(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
+                           int64_t batch_stride_w, const float* U, int64_t batch_stride_u, const int32_t* perm,
+                           const uint8_t* dead, const gptq_params* p, uint8_t* codes, float* scales,
+                           uint8_t* zeros, int32_t* g_idx) {
   if (batch < 1 || d_out < 1 || d_in < gptq::kBlock || d_in % gptq::kBlock != 0 || !valid_dtype(w_dtype))
     return GPTQ_ERR_INVALID_ARG;
   if (W == nullptr || U == nullptr || perm == nullptr || dead == nullptr || codes == nullptr || scales == nullptr ||
@@ -175,9 +176,36 @@ gptq_status gptq_quantize_layer(int batch, int d_out, int d_in, gptq_dtype w_dty
   if (batch > 1 && (batch_stride_w < ldw * d_out || batch_stride_u < dd || batch_stride_u % 4 != 0))
     return GPTQ_ERR_INVALID_ARG;
   if (!aligned(U, 16)) return GPTQ_ERR_INVALID_ARG;
+  return GPTQ_OK;
+}
+}  // namespace
+
+gptq_status gptq_quantize_layer(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
+                                int64_t batch_stride_w, const float* U, int64_t batch_stride_u, const int32_t* perm,
+                                const uint8_t* dead, const gptq_params* p, uint8_t* codes, float* scales,
+                                uint8_t* zeros, int32_t* g_idx, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  const gptq_status st = check_quantize(batch, d_out, d_in, w_dtype, W, ldw, batch_stride_w, U, batch_stride_u, perm,
+                                        dead, p, codes, scales, zeros, g_idx);
+  if (st != GPTQ_OK) return st;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
   return gptq::quantize_enqueue(batch, d_out, d_in, w_dtype, W, ldw, batch > 1 ? batch_stride_w : ldw * d_out, U,
                                 batch > 1 ? batch_stride_u : dd, perm, dead, *p, codes, scales, zeros, g_idx,
                                 workspace, workspace_bytes, stream);
+}
+
+gptq_status gptq_quantize_layer_noalloc(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W,
+                                        int64_t ldw, int64_t batch_stride_w, const float* U, int64_t batch_stride_u,
+                                        const int32_t* perm, const uint8_t* dead, const gptq_params* p,
+                                        uint8_t* codes, float* scales, uint8_t* zeros, int32_t* g_idx,
+                                        hipStream_t stream) {
+  const gptq_status st = check_quantize(batch, d_out, d_in, w_dtype, W, ldw, batch_stride_w, U, batch_stride_u, perm,
+                                        dead, p, codes, scales, zeros, g_idx);
+  if (st != GPTQ_OK) return st;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  return gptq::quantize_noalloc_enqueue(batch, d_out, d_in, w_dtype, W, ldw,
+                                        batch > 1 ? batch_stride_w : ldw * d_out, U, batch > 1 ? batch_stride_u : dd,
+                                        perm, dead, *p, codes, scales, zeros, g_idx, stream);
 }
 
 gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const uint8_t* codes, const float* scales,
@@ -215,6 +243,7 @@ const char* gptq_status_string(gptq_status s) {
     case GPTQ_ERR_HIP: return "HIP runtime error";
     case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
     case GPTQ_ERR_UNSUPPORTED: return "unsupported parameters";
+    case GPTQ_ERR_TOO_LARGE: return "problem exceeds the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }

@@ -22,10 +22,17 @@
 //                    right] as fp32-accurate matrix-core products (split-bf16 when large),
 //                    Err [d_out, d_in] in processing order.
 //   unpermute:       codes back to original column order; g_idx.
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
 #include "common.h"
+
+// Scratch of the allocation-free entry point (gptq_quantize_layer_noalloc): a fixed array
+// of device memory, one per GPU that the library runs on, held until the process ends.
+// Host code never uses the array's name as an address: its device address is looked up
+// once per device (scratch_address below) and kept.
+static __device__ __align__(256) unsigned char scratch[GPTQ_NOALLOC_SCRATCH_BYTES];
 
 namespace gptq {
 namespace {
@@ -524,12 +531,13 @@ struct SweepArgs {
   uint8_t* zeros;
   uint8_t* codes_p;
   float* err;
+  bool timed;            // the launch-timing hook may bracket these launches
 };
 
 template <int G, int NT, int LPR, bool kStatic>
 gptq_status launch_sweep(dim3 grid, hipStream_t stream, const SweepArgs& a, int blk) {
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  timing_pair(GPTQ_TIME_SWEEP, &ev0, &ev1);
+  if (a.timed) timing_pair(GPTQ_TIME_SWEEP, &ev0, &ev1);
   if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
   GPTQ_LAUNCH((block_sweep_kernel<G, NT, LPR, kStatic>), grid, dim3(NT), 0, stream, a.Wp, a.U, a.bsu, a.d_out, a.d_in,
               blk, a.maxq, a.sym, a.perm, a.gsz, a.scales, a.zeros, a.codes_p, a.err);
@@ -591,7 +599,7 @@ gptq_status sweep_range(int b0, int b1, int G, bool stat, const SweepShape& sg, 
   g.sC = static_cast<int64_t>(a.d_out) * d_in;
   g.alpha = -1.0f; g.beta = 1.0f; g.transB = 0; g.flags = 0; g.batch = batch; g.role = 1;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  timing_pair(GPTQ_TIME_LAZY_GEMM, &ev0, &ev1);
+  if (a.timed) timing_pair(GPTQ_TIME_LAZY_GEMM, &ev0, &ev1);
   if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
   if ((st = gemm_f32(g, stream)) != GPTQ_OK) return st;
   if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
@@ -605,10 +613,12 @@ size_t quantize_workspace(int batch, int d_out, int d_in, const gptq_params&) {
   return carve(nullptr, batch, d_out, d_in).bytes + 256;
 }
 
-gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
-                             int64_t bsw, const float* U, int64_t bsu, const int32_t* perm, const uint8_t* dead,
-                             const gptq_params& p, uint8_t* codes, float* scales, uint8_t* zeros, int32_t* g_idx,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+gptq_status quantize_impl(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
+                          int64_t bsw, const float* U, int64_t bsu, const int32_t* perm, const uint8_t* dead,
+                          const gptq_params& p, uint8_t* codes, float* scales, uint8_t* zeros, int32_t* g_idx,
+                          void* ws, size_t ws_bytes, hipStream_t stream, bool timed) {
   QuantWs w = carve(ws, batch, d_out, d_in);
   if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_ERR_WORKSPACE;
   const int G = p.group_size == -1 ? 0 : p.group_size;
@@ -684,7 +694,7 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
     }
   }
   const SweepShape sg = sweep_shape(G, stat, batch, d_out);
-  const SweepArgs sa{w.Wp, U, bsu, d_out, d_in, maxq, p.sym, perm, G, scales, zeros, w.codes_p, w.err};
+  const SweepArgs sa{w.Wp, U, bsu, d_out, d_in, maxq, p.sym, perm, G, scales, zeros, w.codes_p, w.err, timed};
   const gptq_status st = sweep_range(0, d_in / kBlock, stat ? 0 : G, stat, sg, stream, batch, sa);
   if (st != GPTQ_OK) return st;
   {
@@ -704,6 +714,50 @@ gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype,
     if (st != GPTQ_OK) return st;
   }
   return GPTQ_OK;
+}
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+gptq_status scratch_address(void** out) {
+  int dev = 0;
+  GPTQ_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kScratchDevices) return GPTQ_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(::scratch)) != hipSuccess || ptr == nullptr) return GPTQ_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+gptq_status quantize_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W, int64_t ldw,
+                             int64_t bsw, const float* U, int64_t bsu, const int32_t* perm, const uint8_t* dead,
+                             const gptq_params& p, uint8_t* codes, float* scales, uint8_t* zeros, int32_t* g_idx,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  return quantize_impl(batch, d_out, d_in, w_dtype, W, ldw, bsw, U, bsu, perm, dead, p, codes, scales, zeros, g_idx,
+                       ws, ws_bytes, stream, true);
+}
+
+// The same kernels with the scratch array as the workspace.  Everything the kernels read
+// from the scratch they have written earlier in the same call (the permuted weights, the
+// errors, the processing-order codes, the inverse permutation), so nothing needs clearing.
+// No event is recorded (the timing hook would create events).
+gptq_status quantize_noalloc_enqueue(int batch, int d_out, int d_in, gptq_dtype w_dtype, const void* W,
+                                     int64_t ldw, int64_t bsw, const float* U, int64_t bsu, const int32_t* perm,
+                                     const uint8_t* dead, const gptq_params& p, uint8_t* codes, float* scales,
+                                     uint8_t* zeros, int32_t* g_idx, hipStream_t stream) {
+  if (carve(nullptr, batch, d_out, d_in).bytes > kNoAllocScratchBytes) return GPTQ_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (const gptq_status st = scratch_address(&ws); st != GPTQ_OK) return st;
+  return quantize_impl(batch, d_out, d_in, w_dtype, W, ldw, bsw, U, bsu, perm, dead, p, codes, scales, zeros, g_idx,
+                       ws, kNoAllocScratchBytes, stream, false);
 }
 
 }  // namespace gptq

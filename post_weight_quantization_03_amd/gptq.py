@@ -22,9 +22,12 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so
 _lib = None
 
 GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_HIP, GPTQ_ERR_WORKSPACE, GPTQ_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+GPTQ_ERR_TOO_LARGE = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 WS_HESSIAN, WS_PREPARE, WS_QUANTIZE = 0, 1, 2
 
-EXPORTED = ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_int4",
+EXPORTED = ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
+            "gptq_pack_int4",
             "gptq_workspace_size", "gptq_status_string", "gptq_version", "gptq_timing_enable", "gptq_timing_read")
 
 
@@ -82,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.gptq_prepare_hinv.argtypes = [i32, i32, vp, i64, vp, ctypes.POINTER(_Params), vp, i64, vp, vp, vp, sz, vp]
     L.gptq_quantize_layer.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, vp, vp, ctypes.POINTER(_Params),
                                       vp, vp, vp, vp, vp, sz, vp]
+    L.gptq_quantize_layer_noalloc.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, vp, vp,
+                                              ctypes.POINTER(_Params), vp, vp, vp, vp, vp]
     L.gptq_pack_int4.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.gptq_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.POINTER(_Params)]
     L.gptq_workspace_size.restype = sz
@@ -91,8 +96,8 @@ def lib() -> ctypes.CDLL:
     L.gptq_version.restype = ctypes.c_char_p
     L.gptq_timing_enable.argtypes = [i32]
     L.gptq_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for name in ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack_int4",
-                 "gptq_timing_enable", "gptq_timing_read"):
+    for name in ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
+                 "gptq_pack_int4", "gptq_timing_enable", "gptq_timing_read"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -217,6 +222,41 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
                                      d_in * d_in, perm.data_ptr(), dead.data_ptr(), ctypes.byref(p),
                                      codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), g_idx.data_ptr(),
                                      ws.data_ptr(), ws.numel(), _stream(stream)), "gptq_quantize_layer")
+    return codes, scales, zeros, g_idx
+
+
+def quantize_layer_noalloc(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: torch.Tensor, params: Params,
+                           out=None, stream=None):
+    """gptq_quantize_layer_noalloc: the same results as :func:`quantize_layer` with the
+    library's fixed device scratch instead of a workspace.  ``out`` = (codes, scales,
+    zeros, g_idx) preallocated by the caller (shapes as returned by quantize_layer);
+    without it they are allocated here, but the C call itself never allocates."""
+    Wb = _batched(W, 2)
+    batch, d_out, d_in = Wb.shape
+    if W.dtype not in _DT:
+        raise TypeError("W must be fp32/bf16/fp16")
+    if Wb.stride(2) != 1 or not U.is_contiguous() or not perm.is_contiguous() or not dead.is_contiguous():
+        raise ValueError("W rows, U, perm and dead must be contiguous")
+    ng = params.n_groups(d_in)
+    lead = W.shape[:-2]
+    if out is None:
+        out = (torch.empty(*lead, d_out, d_in, dtype=torch.uint8, device=W.device),
+               torch.empty(*lead, ng, d_out, dtype=torch.float32, device=W.device),
+               torch.empty(*lead, ng, d_out, dtype=torch.uint8, device=W.device),
+               torch.empty(*lead, d_in, dtype=torch.int32, device=W.device))
+        _keep_for(stream, *out)
+    codes, scales, zeros, g_idx = out
+    want = [((*lead, d_out, d_in), torch.uint8), ((*lead, ng, d_out), torch.float32),
+            ((*lead, ng, d_out), torch.uint8), ((*lead, d_in), torch.int32)]
+    for t, (shape, dt) in zip(out, want):
+        if tuple(t.shape) != tuple(shape) or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"output tensor must be contiguous {dt} of shape {shape}")
+    p = params.c()
+    _check(lib().gptq_quantize_layer_noalloc(batch, d_out, d_in, _DT[W.dtype], Wb.data_ptr(), Wb.stride(1),
+                                             Wb.stride(0) if batch > 1 else d_out * Wb.stride(1), U.data_ptr(),
+                                             d_in * d_in, perm.data_ptr(), dead.data_ptr(), ctypes.byref(p),
+                                             codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), g_idx.data_ptr(),
+                                             _stream(stream)), "gptq_quantize_layer_noalloc")
     return codes, scales, zeros, g_idx
 
 

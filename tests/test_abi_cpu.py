@@ -42,7 +42,7 @@ def test_timing_hook_without_launches():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert gptq.status_string(s)
     assert "positive definite" in gptq.status_string(gptq.GPTQ_ERR_NOT_SPD)
 
@@ -90,6 +90,12 @@ def test_invalid_arguments_are_rejected_before_any_launch():
                                      null, 0, null) == code, kw
     # pack: d_out not a multiple of 8
     assert L.gptq_pack_int4(1, 12, 128, 1, 8, 8, 8, 8, 8, 8, null) == bad
+    # allocation-free quantize: the same argument checks, then the size limit of its fixed
+    # scratch (9 bytes per weight), both before any device call
+    assert L.gptq_quantize_layer_noalloc(1, 8, 100, 1, 16, 128, 0, 16, 0, 8, 8, ctypes.byref(p), 8, 8, 8, 8,
+                                         null) == bad
+    assert L.gptq_quantize_layer_noalloc(1, 8192, 8192, 1, 16, 8192, 0, 16, 0, 16, 16, ctypes.byref(p), 16, 16, 16,
+                                         16, null) == gptq.GPTQ_ERR_TOO_LARGE
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
