@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="tokens per accumulate call (0 = all at once)")
     ap.add_argument("--bits", type=int, default=0, help="override the workload's bit width (e.g. 3 for moe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-serve", action="store_true", help="skip the W4A16 decode measurement")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
                     help="calibration tokens the CPU oracle processes (its Hessian time is scaled up)")
     ap.add_argument("--cpu-sample-rows", type=int, default=64,
@@ -143,6 +144,39 @@ def cpu_baseline(spec, Ws, Xs, sample_tokens: int, sample_rows: int, sample_dim:
                         f"measured {t3 - t0:.1f} s"),
                 blas_threads=blas_threads, ms_per_layer=full * 1e3, stage_s={k: round(v, 3) for k, v in t.items()},
                 stage_s_scaled={k: round(v, 2) for k, v in scaled.items()})
+
+
+def w4a16_decode(gptq, torch, qweight, qzeros, scales_f16, g_idx, n_groups, rows, dtype, reps):
+    """Decode-time W4A16 product on the benchmark layer's own checkpoint: repack once, then
+    time gptq_w4a16_matmul with ``rows`` activation rows over enough copies of the packed
+    weights (rotated) that no copy is still in the 256 MB last-level cache when it is read
+    again.  Algorithmic bytes per call: qweight, scales, qzeros, X and Y once."""
+    d_in = qweight.shape[-2] * 8
+    d_out = qweight.shape[-1]
+    qs, order = gptq.w4a16_repack(qweight, g_idx, n_groups)
+    per = qs.numel() * 4 + scales_f16.numel() * 2 + qzeros.numel() * 4
+    copies = max(2, -(-(768 << 20) // per))
+    sets = [(qs.clone(), qzeros.clone(), scales_f16.clone()) for _ in range(copies)]
+    X = torch.randn(rows, d_in, device=qs.device).to(dtype)
+    Y = torch.empty(rows, d_out, dtype=torch.float32, device=qs.device)
+    for q_, z_, s_ in sets[:2]:
+        gptq.w4a16_matmul(X, q_, z_, s_, order, out=Y)
+    torch.cuda.synchronize()
+    gptq.timing_enable(True)
+    gptq.timing_read(gptq.TIME_W4A16)
+    for i in range(reps):
+        q_, z_, s_ = sets[i % copies]
+        gptq.w4a16_matmul(X, q_, z_, s_, order, out=Y)
+    torch.cuda.synchronize()
+    gptq.timing_enable(False)
+    total, n = gptq.timing_read(gptq.TIME_W4A16)
+    call_ms = total / max(n, 1)
+    alg = per + rows * d_in * 2 + rows * d_out * 4
+    gbs = alg / (call_ms / 1e3) / 1e9 if call_ms > 0 else 0.0
+    return dict(bound="hbm", kernel="w4a16_kernel + w4a16_reduce_kernel", rows=rows, achieved=round(gbs, 1),
+                peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                launch_ms=round(call_ms, 5), calls=n, bytes_per_call=alg, weight_copies=copies,
+                tflops=round(2.0 * rows * d_in * d_out / (call_ms / 1e3) / 1e12, 2) if call_ms > 0 else 0.0)
 
 
 def main():
@@ -311,6 +345,16 @@ def main():
                                           achieved=round(pk_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                           frac=round(pk_gbs / PEAK_HBM_GBS, 4), traffic=None,
                                           launch_ms=round(pk_ms, 5), launches=pk_n, bytes_per_launch=pack_bytes)
+    if packs and spec.bits == 4 and spec.batch == 1 and spec.dtype in ("bf16", "f16") and not args.no_serve:
+        # the serving product of the layer just quantized: its packed checkpoint from one more step
+        U, perm, dead = gptq.prepare_hinv(H, key, p, workspace=ws_p)
+        codes, scales, zeros, g_idx = gptq.quantize_layer(W, U, perm, dead, p, workspace=ws_q)
+        qw, qz, sf = gptq.pack_int4(codes, scales, zeros)
+        ng = scales.shape[-2]
+        xdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float16
+        out_extra["roofline_w4a16_decode"] = [
+            w4a16_decode(gptq, torch, qw, qz, sf, g_idx, ng, rows, xdt, reps=200) for rows in (1, 16)]
+        del U, codes, qw, qz, sf
     out = dict(metric=METRIC, value=round(value, 4), unit="Gweights/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype=f"{spec.dtype}->f32", data="synthetic",

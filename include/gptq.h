@@ -89,7 +89,13 @@ typedef struct {
 } gptq_params;
 
 /* Which call a workspace is sized for. */
-typedef enum { GPTQ_WS_HESSIAN = 0, GPTQ_WS_PREPARE = 1, GPTQ_WS_QUANTIZE = 2 } gptq_ws_call;
+typedef enum {
+  GPTQ_WS_HESSIAN = 0,
+  GPTQ_WS_PREPARE = 1,
+  GPTQ_WS_QUANTIZE = 2,
+  GPTQ_WS_W4A16_REPACK = 3,
+  GPTQ_WS_W4A16 = 4
+} gptq_ws_call;
 
 /*
  * Hessian accumulation — "Same Ruler, Smarter Placement: GPTQ", 1.4 (H = 2 X X^T, the
@@ -113,6 +119,27 @@ gptq_status gptq_accumulate_hessian(int batch, int d_in, int64_t n_tokens, gptq_
                                     float* H, int64_t batch_stride_h, double* diag_key,
                                     int64_t* n_seen, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/*
+ * Grouped Hessian accumulation — the same sums as gptq_accumulate_hessian for `batch`
+ * problems whose calibration tokens lie in one token-major buffer X [total_tokens, d_in]
+ * (row stride ldx), problem e owning rows token_offsets[e] .. token_offsets[e + 1] - 1: the
+ * tokens a mixture-of-experts router sends to expert e ("GPTQ Architecture, in depth",
+ * "Failure modes": experts that receive few tokens are starved, so their counts are
+ * reported).  token_offsets: DEVICE int64 [batch + 1]; each range is clamped to [0,
+ * total_tokens] (a decreasing pair is empty) and to its first max_tokens_per_problem rows,
+ * which sizes the launch (gptq_workspace_size(GPTQ_WS_HESSIAN, batch, 0, d_in,
+ * max_tokens_per_problem, ...)).  For every problem: H[e] += 2 X_e^T X_e, diag_key[e] +=
+ * 2 sum x^2 (fp64), n_seen[e] += the number of rows accumulated (0 for a problem that got
+ * no token: its H stays 0 and every input is then dead).  One launch per kernel covers
+ * all problems.  Requires d_in % 8 == 0 and a 16-byte aligned X.
+ */
+gptq_status gptq_accumulate_hessian_grouped(int batch, int d_in, int64_t total_tokens,
+                                            int64_t max_tokens_per_problem, gptq_dtype x_dtype,
+                                            const void* X, int64_t ldx, const int64_t* token_offsets,
+                                            float* H, int64_t batch_stride_h, double* diag_key,
+                                            int64_t* n_seen, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Inverse-Hessian factor — "GPTQ Architecture, in depth", "The algorithm in code"
@@ -211,9 +238,58 @@ gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const u
                            const float* scales, const uint8_t* zeros, int32_t* qweight,
                            int32_t* qzeros, uint16_t* scales_f16, hipStream_t stream);
 
+/*
+ * Serving layout for the W4A16 product — "Same Ruler, Smarter Placement: GPTQ", 1.9 (with
+ * act-order the weight columns are permuted and the activations are permuted the same way
+ * at inference time) and "GPTQ Architecture, in depth", "Groups, act-order and other
+ * knobs" (groups formed in permuted order scatter the scale reads).
+ *
+ * For every problem e < batch (qweight and g_idx as written by gptq_pack_int4 and
+ * gptq_quantize_layer, batch strides the dense sizes):
+ *   order[e]     int32 [d_in]: the inputs sorted by group, g_idx ascending, ties by
+ *                ascending input index (the position of input c is g_idx[c] * gs + the
+ *                number of earlier inputs of its group, gs = d_in / n_groups)
+ *   qweight_s[e] int32 [d_in/8, d_out]: qweight with its inputs in that order (nibble t of
+ *                word i holds input order[8 i + t])
+ * Every group must have exactly gs members and every g_idx lie in [0, n_groups); the
+ * call waits for its kernels to read that check and returns GPTQ_ERR_INVALID_ARG
+ * otherwise (outputs then unspecified).  workspace: at least
+ * gptq_workspace_size(GPTQ_WS_W4A16_REPACK, ...) bytes of device memory (a flag).
+ * Requires d_out % 8 == 0, d_in % 8 == 0 and n_groups dividing d_in.  When g_idx[c] = c /
+ * gs already (static groups, or no act-order), order is the identity and qweight_s equals
+ * qweight: gptq_w4a16_matmul then takes the checkpoint's qweight with order = NULL.
+ */
+gptq_status gptq_w4a16_repack(int batch, int d_out, int d_in, int n_groups, const int32_t* qweight,
+                              const int32_t* g_idx, int32_t* qweight_s, int32_t* order,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * W4A16 product — "GPTQ Architecture, in depth", "Packing, tooling and serving": 4-bit
+ * weights stay packed and are dequantized in registers right before the product with
+ * 16-bit activations (decode is bound by reading the weights):
+ *   Y[r, o] = sum_c X[r, c] * scale[g_idx[c], o] * (code[o, c] - zero[g_idx[c], o])
+ * X [m, d_in] bf16 or fp16 bits, row stride ldx (>= d_in); Y fp32 [m, d_out], row stride
+ * ldy (>= d_out, a multiple of 4, Y 16-byte aligned).  qweight_s / order from
+ * gptq_w4a16_repack (order = NULL: qweight_s is in input order and g_idx[c] = c / gs);
+ * qzeros int32 [n_groups, d_out/8] and scales_f16 [n_groups, d_out] as written by
+ * gptq_pack_int4.  The codes enter 16-bit matrix-core products exactly; the group's scale
+ * and zero are applied in fp32 once per group (sums in fp32).  Rows are processed 16 at a
+ * time.  workspace: gptq_workspace_size(GPTQ_WS_W4A16, batch = 1, d_out, d_in,
+ * n_tokens_hint = m, p with the group size) bytes (K-split partial sums; 256 when unsplit).
+ * Requires m >= 1, d_out % 8 == 0, d_in % 128 == 0, a group size gs = d_in / n_groups of
+ * 32, 64 or 128, or n_groups = 1 (one grid per row), and qweight_s 16-byte aligned.
+ */
+gptq_status gptq_w4a16_matmul(int m, int d_out, int d_in, int n_groups, gptq_dtype x_dtype,
+                              const void* X, int64_t ldx, const int32_t* qweight_s,
+                              const int32_t* order, const int32_t* qzeros,
+                              const uint16_t* scales_f16, float* Y, int64_t ldy, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace the given call needs (0 on invalid arguments).  For
  * GPTQ_WS_HESSIAN `d_out` is ignored and `n_tokens_hint` is the largest n_tokens per call
- * (it only sizes the split over tokens); for the other calls it is ignored. */
+ * (it only sizes the split over tokens); for GPTQ_WS_W4A16 `n_tokens_hint` is the number
+ * of activation rows m and p->group_size the group size (-1: one grid per row); for the
+ * other calls it is ignored. */
 size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
                            int64_t n_tokens_hint, const gptq_params* p);
 
@@ -223,6 +299,7 @@ size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
  *   GPTQ_TIME_LAZY_GEMM  every lazy trailing-update product of gptq_quantize_layer
  *   GPTQ_TIME_SWEEP      every 128-column sweep kernel of gptq_quantize_layer
  *   GPTQ_TIME_PACK       the packing kernels of one gptq_pack_int4 call (one pair per call)
+ *   GPTQ_TIME_W4A16      the kernels of one gptq_w4a16_matmul call (one pair per call)
  * While enabled (on != 0), every such launch is bracketed by a pair of HIP events recorded
  * on the call's stream immediately around it.  gptq_timing_read waits for the recorded
  * events of one class, returns their summed elapsed milliseconds and the number of
@@ -234,7 +311,8 @@ typedef enum {
   GPTQ_TIME_SYRK = 0,
   GPTQ_TIME_LAZY_GEMM = 1,
   GPTQ_TIME_SWEEP = 2,
-  GPTQ_TIME_PACK = 3
+  GPTQ_TIME_PACK = 3,
+  GPTQ_TIME_W4A16 = 4
 } gptq_timed_kernel;
 gptq_status gptq_timing_enable(int on);
 gptq_status gptq_timing_read(gptq_timed_kernel which, double* total_ms, int64_t* launches);

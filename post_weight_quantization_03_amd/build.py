@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq.so")
 
-SOURCES = ["gptq_abi.hip", "hessian.hip", "gemm.hip", "prepare.hip", "quantize.hip", "pack.hip"]
+SOURCES = ["gptq_abi.hip", "hessian.hip", "gemm.hip", "prepare.hip", "quantize.hip", "pack.hip", "serve.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 

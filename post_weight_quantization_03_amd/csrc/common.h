@@ -69,9 +69,11 @@ struct Carver {
 
 // Internal entry points of the translation units (host side).
 namespace gptq {
+// offsets (device, batch + 1 entries) or null: see problem_rows in hessian.hip.
 gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_dtype, const void* X,
-                            int64_t ldx, int64_t bsx, float* H, int64_t bsh, double* diag_key,
-                            int64_t* n_seen, void* ws, size_t ws_bytes, hipStream_t stream);
+                            int64_t ldx, int64_t bsx, const int64_t* offsets, int64_t total_rows, float* H,
+                            int64_t bsh, double* diag_key, int64_t* n_seen, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 size_t hessian_workspace(int batch, int d_in, int64_t n_tokens);
 
 gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, const double* diag_key,
@@ -93,13 +95,22 @@ gptq_status quantize_noalloc_enqueue(int batch, int d_out, int d_in, gptq_dtype 
                                      const uint8_t* dead, const gptq_params& p, uint8_t* codes, float* scales,
                                      uint8_t* zeros, int32_t* g_idx, hipStream_t stream);
 
+size_t serve_workspace(int m, int d_out, int d_in, int n_groups);
+gptq_status repack_enqueue(int batch, int d_out, int d_in, int n_groups, const int32_t* qweight,
+                           const int32_t* g_idx, int32_t* qweight_s, int32_t* order, int* flag,
+                           hipStream_t stream);
+gptq_status serve_enqueue(int m, int d_out, int d_in, int n_groups, gptq_dtype x_dtype, const void* X, int64_t ldx,
+                          const int32_t* order, const int32_t* qweight, const int32_t* qzeros,
+                          const uint16_t* scales, float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uint8_t* codes,
                          const float* scales, const uint8_t* zeros, int32_t* qweight, int32_t* qzeros,
                          uint16_t* scales_f16, hipStream_t stream);
 
 // Launch timing (gptq_timing_enable / gptq_timing_read): returns the event pair to record
 // around the next launch of the given class, or nulls when timing is off.
-constexpr int kTimedKinds = 4;
+constexpr int kTimedKinds = 5;
 void timing_pair(gptq_timed_kernel kind, hipEvent_t* start, hipEvent_t* stop);
 
 // A second stream per device for work that can overlap the caller's stream; two events

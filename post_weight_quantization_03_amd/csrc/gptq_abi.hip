@@ -133,8 +133,30 @@ gptq_status gptq_accumulate_hessian(int batch, int d_in, int64_t n_tokens, gptq_
   const int64_t vec = 16 / static_cast<int64_t>(dtype_bytes(x_dtype));
   if (X == nullptr || ldx < d_in || ldx % vec != 0 || !aligned(X, 16)) return GPTQ_ERR_INVALID_ARG;
   if (batch > 1 && (batch_stride_x < ldx * n_tokens || batch_stride_x % vec != 0)) return GPTQ_ERR_INVALID_ARG;
-  return gptq::hessian_enqueue(batch, d_in, n_tokens, x_dtype, X, ldx, batch_stride_x, H,
+  return gptq::hessian_enqueue(batch, d_in, n_tokens, x_dtype, X, ldx, batch_stride_x, nullptr, 0, H,
                                batch > 1 ? batch_stride_h : dd, diag_key, n_seen, workspace, workspace_bytes,
+                               stream);
+}
+
+gptq_status gptq_accumulate_hessian_grouped(int batch, int d_in, int64_t total_tokens,
+                                            int64_t max_tokens_per_problem, gptq_dtype x_dtype, const void* X,
+                                            int64_t ldx, const int64_t* token_offsets, float* H,
+                                            int64_t batch_stride_h, double* diag_key, int64_t* n_seen,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 1 || d_in < 8 || d_in % 8 != 0 || total_tokens < 0 || max_tokens_per_problem < 0 ||
+      !valid_dtype(x_dtype))
+    return GPTQ_ERR_INVALID_ARG;
+  if (H == nullptr || diag_key == nullptr || n_seen == nullptr || token_offsets == nullptr ||
+      !aligned(token_offsets, 8))
+    return GPTQ_ERR_INVALID_ARG;
+  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+  if (batch_stride_h < dd && batch > 1) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned(H, 16) || (batch > 1 && batch_stride_h % 4 != 0)) return GPTQ_ERR_INVALID_ARG;
+  if (max_tokens_per_problem == 0 || total_tokens == 0) return GPTQ_OK;
+  const int64_t vec = 16 / static_cast<int64_t>(dtype_bytes(x_dtype));
+  if (X == nullptr || ldx < d_in || ldx % vec != 0 || !aligned(X, 16)) return GPTQ_ERR_INVALID_ARG;
+  return gptq::hessian_enqueue(batch, d_in, max_tokens_per_problem, x_dtype, X, ldx, 0, token_offsets, total_tokens,
+                               H, batch > 1 ? batch_stride_h : dd, diag_key, n_seen, workspace, workspace_bytes,
                                stream);
 }
 
@@ -219,6 +241,41 @@ gptq_status gptq_pack_int4(int batch, int d_out, int d_in, int n_groups, const u
   return gptq::pack_enqueue(batch, d_out, d_in, n_groups, codes, scales, zeros, qweight, qzeros, scales_f16, stream);
 }
 
+gptq_status gptq_w4a16_repack(int batch, int d_out, int d_in, int n_groups, const int32_t* qweight,
+                              const int32_t* g_idx, int32_t* qweight_s, int32_t* order, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 1 || d_out < 8 || d_out % 8 != 0 || d_in < 8 || d_in % 8 != 0 || n_groups < 1 || d_in % n_groups != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  if (qweight == nullptr || g_idx == nullptr || qweight_s == nullptr || order == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < sizeof(int) || !aligned(workspace, 4)) return GPTQ_ERR_WORKSPACE;
+  int* flag = static_cast<int*>(workspace);
+  gptq_status st = gptq::repack_enqueue(batch, d_out, d_in, n_groups, qweight, g_idx, qweight_s, order, flag, stream);
+  if (st != GPTQ_OK) return st;
+  int bad = 0;
+  GPTQ_HIP_TRY(hipMemcpyAsync(&bad, flag, sizeof(int), hipMemcpyDeviceToHost, stream));
+  GPTQ_HIP_TRY(hipStreamSynchronize(stream));
+  return bad ? GPTQ_ERR_INVALID_ARG : GPTQ_OK;
+}
+
+gptq_status gptq_w4a16_matmul(int m, int d_out, int d_in, int n_groups, gptq_dtype x_dtype, const void* X,
+                              int64_t ldx, const int32_t* qweight_s, const int32_t* order, const int32_t* qzeros,
+                              const uint16_t* scales_f16, float* Y, int64_t ldy, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (m < 1 || d_out < 8 || d_out % 8 != 0 || d_in < 128 || d_in % 128 != 0 || n_groups < 1 ||
+      d_in % n_groups != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  const int gs = d_in / n_groups;
+  if (!(n_groups == 1 || gs == 32 || gs == 64 || gs == 128)) return GPTQ_ERR_UNSUPPORTED;
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F16) return GPTQ_ERR_INVALID_ARG;
+  if (X == nullptr || qweight_s == nullptr || qzeros == nullptr || scales_f16 == nullptr || Y == nullptr)
+    return GPTQ_ERR_INVALID_ARG;
+  if (ldx < d_in || ldy < d_out || ldy % 4 != 0 || !aligned(Y, 16) || !aligned(qweight_s, 16) ||
+      !aligned(scales_f16, 8))
+    return GPTQ_ERR_INVALID_ARG;
+  return gptq::serve_enqueue(m, d_out, d_in, n_groups, x_dtype, X, ldx, order, qweight_s, qzeros, scales_f16, Y, ldy,
+                             workspace, workspace_bytes, stream);
+}
+
 size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in, int64_t n_tokens_hint,
                            const gptq_params* p) {
   switch (which) {
@@ -230,6 +287,14 @@ size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in, i
     case GPTQ_WS_QUANTIZE: {
       if (p == nullptr) return 0;
       return gptq::quantize_workspace(batch, d_out, d_in, *p);
+    }
+    case GPTQ_WS_W4A16_REPACK:
+      return 256;
+    case GPTQ_WS_W4A16: {
+      if (p == nullptr || n_tokens_hint < 1 || n_tokens_hint > INT32_MAX) return 0;
+      const int ng = p->group_size == -1 ? 1 : (p->group_size > 0 && d_in % p->group_size == 0 ? d_in / p->group_size : 0);
+      if (ng == 0) return 0;
+      return gptq::serve_workspace(static_cast<int>(n_tokens_hint), d_out, d_in, ng);
     }
   }
   return 0;

@@ -45,41 +45,60 @@ constexpr int NBUF = 2;                   // LDS stage buffers per operand
 constexpr int SYRK_WAVES = 8;
 constexpr int kMinTokensPerSplit = 2048;
 
-// (I, J) of lower tile t of an nt x nt tile grid, in an order that keeps concurrent tiles
-// on few channel panels: super-rows of 4 tile rows, within one super-row column chunks of 8
-// tiles, within a chunk row by row.  32 consecutive tiles (one round of an XCD's CUs) then
-// read 4 + 8 = 12 panels; row by row they would read up to 33 on a wide layer.  Scalar
-// loops of at most nt / 4 and nt / 8 iterations.
-__device__ __forceinline__ void blocked_tile_coords(int t, int nt, int& I, int& J) {
-  int r0 = 0;
-  for (;;) {   // super-row
-    const int nr = min(4, nt - r0);
-    // tiles of rows r0 .. r0 + nr - 1: sum of (I + 1)
-    const int cnt = nr * (r0 + 1) + nr * (nr - 1) / 2;
-    if (t < cnt || r0 + nr >= nt) break;
-    t -= cnt;
-    r0 += 4;
+// Lower tiles (J <= I) of the tile rectangle rows [r0, r1) x columns [c0, c1).
+__device__ __forceinline__ int lower_count(int r0, int r1, int c0, int c1) {
+  int n = 0;
+  for (int i = r0; i < r1; ++i) n += max(0, min(c1, i + 1) - c0);
+  return n;
+}
+
+// (I, J) of lower tile t of an nt x nt tile grid, in an order whose aligned runs of 256
+// tiles (one round of one workgroup per CU on all 256 CUs) stay inside one block of 16 x
+// 16 tiles, and whose runs of 32 (the share of one XCD in a round) stay inside one 4 x 8
+// sub-block of it: super-blocks of 16 x 16 tiles row by row, inside a super-block its 8
+// sub-blocks (4 tile rows x 8 tile columns) row by row, inside a sub-block tiles row by
+// row.  A round then reads 32 channel panels (16 + 16) for up to 256 tiles, all from one
+// token slice, so concurrent workgroups of all XCDs share their panels in the last-level
+// cache; an XCD's 32 tiles share 4 + 8 panels in its L2.  Scalar loops of at most a few
+// dozen iterations.
+__device__ __forceinline__ void round_tile_coords(int t, int nt, int& I, int& J) {
+  const int nsb = (nt + 15) / 16;
+  int A = 0, Bc = 0;
+  for (A = 0; A < nsb; ++A) {
+    bool found = false;
+    for (Bc = 0; Bc <= A; ++Bc) {
+      const int n = lower_count(16 * A, min(16 * A + 16, nt), 16 * Bc, min(16 * Bc + 16, nt));
+      if (t < n) {
+        found = true;
+        break;
+      }
+      t -= n;
+    }
+    if (found) break;
   }
-  const int nr = min(4, nt - r0);
-  for (int c0 = 0;; c0 += 8) {   // column chunk [c0, c0 + 8)
-    int cnt = 0;
-    for (int i = 0; i < nr; ++i) cnt += max(0, min(8, r0 + i + 1 - c0));
-    if (t < cnt || c0 + 8 > r0 + nr - 1) {
-      for (int i = 0; i < nr; ++i) {
-        const int w = max(0, min(8, r0 + i + 1 - c0));
+  const int R0 = 16 * A, R1 = min(R0 + 16, nt), C0 = 16 * Bc, C1 = min(C0 + 16, nt);
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 2; ++b) {
+      const int r0 = R0 + 4 * a, r1 = min(r0 + 4, R1), c0 = C0 + 8 * b, c1 = min(c0 + 8, C1);
+      if (r0 >= r1 || c0 >= c1) continue;
+      const int n = lower_count(r0, r1, c0, c1);
+      if (t >= n) {
+        t -= n;
+        continue;
+      }
+      for (int i = r0; i < r1; ++i) {
+        const int w = max(0, min(c1, i + 1) - c0);
         if (t < w) {
-          I = r0 + i;
+          I = i;
           J = c0 + t;
           return;
         }
         t -= w;
       }
-      I = r0;   // not reached for t < nt (nt + 1) / 2
-      J = 0;
-      return;
     }
-    t -= cnt;
   }
+  I = 0;   // not reached for t < nt (nt + 1) / 2
+  J = 0;
 }
 
 __device__ __forceinline__ void lower_tile_coords(int t, int& I, int& J) {
@@ -89,6 +108,21 @@ __device__ __forceinline__ void lower_tile_coords(int t, int& I, int& J) {
   while (i * (i + 1) / 2 > t) --i;
   I = i;
   J = t - i * (i + 1) / 2;
+}
+
+// Rows of problem e in its activation buffer: [start, start + count).  Without token
+// offsets every problem has n_tokens rows from its own buffer (X + e * bsx).  With offsets
+// (grouped calls: one buffer, problem e owns rows offsets[e] .. offsets[e + 1]) the range
+// is clamped to the buffer's total_rows rows and to n_tokens, the most rows the launch
+// covers per problem, so no access leaves the buffer whatever the offsets hold.
+struct Rows {
+  int64_t start, count;
+};
+__device__ __forceinline__ Rows problem_rows(const int64_t* offsets, int e, int64_t n_tokens, int64_t total_rows) {
+  if (offsets == nullptr) return {0, n_tokens};
+  const int64_t a = min(max(offsets[e], static_cast<int64_t>(0)), total_rows);
+  const int64_t b = min(max(offsets[e + 1], a), total_rows);
+  return {a, min(b - a, n_tokens)};
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -162,28 +196,31 @@ __device__ __forceinline__ int chunk_logical(int t, int p) {
 // slices in order and adds twice the sum to H and its mirror.
 template <bool kF16, int NW>
 __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
-    const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, int d_in,
-    int64_t tokens_per_split, int ksplit, float* __restrict__ partial, int ntiles) {
+    const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, const int64_t* __restrict__ offsets,
+    int64_t total_rows, int d_in, int64_t tokens_per_split, int ksplit, float* __restrict__ partial, int ntiles) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][SBK * ST];
   __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][SBK * ST];
 
-  // (tile, slice) of this workgroup: bijection from the linear id that keeps each XCD's
-  // share contiguous.
+  // (slice, tile) of this workgroup.  Workgroups start in linear order, dealt to the 8
+  // XCDs round-robin (XCD = id % 8), one per CU, so the running ones form a window of about
+  // 256 consecutive ids.  Positions are slice-major; inside each full run of 256 ids, the
+  // workgroup dealt to XCD x in slot s takes position 32 x + s, so every XCD works on 32
+  // consecutive positions (one sub-block of round_tile_coords) of the same token slice.
   const int e = blockIdx.y;
   const int total = ntiles * ksplit;
   const int lin = blockIdx.x;
-  const int xcd = lin & 7, slot = lin >> 3;
-  const int base_n = total >> 3, extra = total & 7;
-  const int idx = xcd * base_n + min(xcd, extra) + slot;
+  const int rnd = lin >> 8, p = lin & 255;
+  const int idx = (rnd + 1) * 256 <= total ? (rnd << 8) + 32 * (p & 7) + (p >> 3) : lin;
   const int split = idx / ntiles;
   const int tile = idx - split * ntiles;
   int I, J;
-  blocked_tile_coords(tile, (d_in + ST - 1) / ST, I, J);
+  round_tile_coords(tile, (d_in + ST - 1) / ST, I, J);
   const bool diag = (I == J);
   const int I0 = I * ST, J0 = J * ST;
+  const Rows pr = problem_rows(offsets, e, n_tokens, total_rows);
   const int64_t t_begin = static_cast<int64_t>(split) * tokens_per_split;
-  const int64_t t_end = min(n_tokens, t_begin + tokens_per_split);
-  const uint16_t* Xe = X + static_cast<int64_t>(e) * bsx;
+  const int64_t t_end = min(pr.count, t_begin + tokens_per_split);   // an empty slice writes a zero tile
+  const uint16_t* Xe = X + static_cast<int64_t>(e) * bsx + pr.start * ldx;
   const bool full_cols = (I0 + ST <= d_in) && (J0 + ST <= d_in);
 
   const int tid = threadIdx.x;
@@ -373,7 +410,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   const int sub = blockIdx.x;  // 16 sub-blocks of 64x64
   const int sm = (sub >> 2) * 64, sn = (sub & 3) * 64;
   int I, J;
-  blocked_tile_coords(tile, (d_in + ST - 1) / ST, I, J);
+  round_tile_coords(tile, (d_in + ST - 1) / ST, I, J);
   const bool diag = (I == J);
   if (diag && sm < sn) return;  // strictly-upper sub-block of a diagonal tile
   const int c4 = 4 * (threadIdx.x & 15), r0 = threadIdx.x >> 4;   // rows r0 + 16 q
@@ -417,22 +454,24 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 
 // fp32 inputs: 64x64 lower tiles, 256 threads with 4x4 outputs each, FMA in fp32.
 __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ X, int64_t ldx,
-                                                       int64_t bsx, int64_t n_tokens, int d_in,
-                                                       float* __restrict__ H, int64_t bsh) {
+                                                       int64_t bsx, int64_t n_tokens,
+                                                       const int64_t* __restrict__ offsets, int64_t total_rows,
+                                                       int d_in, float* __restrict__ H, int64_t bsh) {
   __shared__ float sa[16][64];
   __shared__ float sb[16][64];
   const int e = blockIdx.z;
   int I, J;
   lower_tile_coords(blockIdx.x, I, J);
   const int I0 = I * 64, J0 = J * 64;
-  const float* Xe = X + static_cast<int64_t>(e) * bsx;
+  const Rows pr = problem_rows(offsets, e, n_tokens, total_rows);
+  const float* Xe = X + static_cast<int64_t>(e) * bsx + pr.start * ldx;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4] = {};
-  for (int64_t t0 = 0; t0 < n_tokens; t0 += 16) {
+  for (int64_t t0 = 0; t0 < pr.count; t0 += 16) {
     for (int i = threadIdx.x; i < 16 * 64; i += 256) {
       const int k = i >> 6, c = i & 63;
       const int64_t t = t0 + k;
-      const bool okt = t < n_tokens;
+      const bool okt = t < pr.count;
       sa[k][c] = (okt && I0 + c < d_in) ? Xe[t * ldx + I0 + c] : 0.0f;
       sb[k][c] = (okt && J0 + c < d_in) ? Xe[t * ldx + J0 + c] : 0.0f;
     }
@@ -472,16 +511,18 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
 // squares are exact in fp64).
 template <typename T>
 __global__ __launch_bounds__(256) void channel_energy_kernel(const T* __restrict__ X, int64_t ldx,
-                                                             int64_t bsx, int64_t n_tokens, int d_in,
-                                                             int64_t tokens_per_split,
+                                                             int64_t bsx, int64_t n_tokens,
+                                                             const int64_t* __restrict__ offsets, int64_t total_rows,
+                                                             int d_in, int64_t tokens_per_split,
                                                              double* __restrict__ part) {
   constexpr int V = 16 / sizeof(T);
   const int c0 = (blockIdx.x * 256 + threadIdx.x) * V;
   const int split = blockIdx.y, e = blockIdx.z;
   if (c0 >= d_in) return;
+  const Rows pr = problem_rows(offsets, e, n_tokens, total_rows);
   const int64_t t0 = static_cast<int64_t>(split) * tokens_per_split;
-  const int64_t t1 = min(n_tokens, t0 + tokens_per_split);
-  const T* Xe = X + static_cast<int64_t>(e) * bsx + c0;
+  const int64_t t1 = min(pr.count, t0 + tokens_per_split);
+  const T* Xe = X + static_cast<int64_t>(e) * bsx + pr.start * ldx + c0;
   double acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.0;
@@ -504,7 +545,9 @@ __global__ __launch_bounds__(256) void channel_energy_reduce_kernel(const double
                                                                     int nsplit, int d_in,
                                                                     double* __restrict__ diag_key,
                                                                     int64_t* __restrict__ n_seen,
-                                                                    int64_t n_tokens) {
+                                                                    int64_t n_tokens,
+                                                                    const int64_t* __restrict__ offsets,
+                                                                    int64_t total_rows) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   const int e = blockIdx.y;
   if (c < d_in) {
@@ -513,7 +556,7 @@ __global__ __launch_bounds__(256) void channel_energy_reduce_kernel(const double
     for (int k = 0; k < nsplit; ++k) s += part[(static_cast<int64_t>(e) * nsplit + k) * d_in + c];
     diag_key[static_cast<int64_t>(e) * d_in + c] += 2.0 * s;
   }
-  if (c == 0) n_seen[e] += n_tokens;
+  if (c == 0) n_seen[e] += problem_rows(offsets, e, n_tokens, total_rows).count;
 }
 
 struct HessianPlan {
@@ -597,8 +640,9 @@ size_t hessian_workspace(int batch, int d_in, int64_t n_tokens) {
 }
 
 gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_dtype, const void* X,
-                            int64_t ldx, int64_t bsx, float* H, int64_t bsh, double* diag_key,
-                            int64_t* n_seen, void* ws, size_t ws_bytes, hipStream_t stream) {
+                            int64_t ldx, int64_t bsx, const int64_t* offsets, int64_t total_rows, float* H,
+                            int64_t bsh, double* diag_key, int64_t* n_seen, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
   if (n_tokens == 0) return GPTQ_OK;
   const bool mfma = (x_dtype == GPTQ_BF16 || x_dtype == GPTQ_F16);
   const HessianPlan pl = make_plan(batch, d_in, n_tokens, mfma);
@@ -632,21 +676,21 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     timing_pair(GPTQ_TIME_SYRK, &ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
-      GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
-                  partial, pl.ntiles);
+      GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, offsets,
+                  total_rows, d_in, pl.kchunk, pl.ksplit, partial, pl.ntiles);
     } else {
-      GPTQ_LAUNCH((syrk_mfma_kernel<false, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, d_in, pl.kchunk, pl.ksplit,
-                  partial, pl.ntiles);
+      GPTQ_LAUNCH((syrk_mfma_kernel<false, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, offsets,
+                  total_rows, d_in, pl.kchunk, pl.ksplit, partial, pl.ntiles);
     }
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
     GPTQ_HIP_TRY(hipEventRecord(ss->fork, stream));
     GPTQ_HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
     if (x_dtype == GPTQ_F16) {
       GPTQ_LAUNCH(channel_energy_kernel<F16>, egrid, blk, 0, ss->s, static_cast<const F16*>(X), ldx, bsx, n_tokens,
-                  d_in, pl.echunk, epart);
+                  offsets, total_rows, d_in, pl.echunk, epart);
     } else {
       GPTQ_LAUNCH(channel_energy_kernel<BF16>, egrid, blk, 0, ss->s, static_cast<const BF16*>(X), ldx, bsx,
-                  n_tokens, d_in, pl.echunk, epart);
+                  n_tokens, offsets, total_rows, d_in, pl.echunk, epart);
     }
     GPTQ_HIP_TRY(hipEventRecord(ss->join, ss->s));
     GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
@@ -657,13 +701,13 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     timing_pair(GPTQ_TIME_SYRK, &ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream, static_cast<const float*>(X), ldx, bsx,
-                n_tokens, d_in, H, bsh);
+                n_tokens, offsets, total_rows, d_in, H, bsh);
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
     GPTQ_LAUNCH(channel_energy_kernel<float>, egrid, blk, 0, stream, static_cast<const float*>(X), ldx, bsx, n_tokens,
-                d_in, pl.echunk, epart);
+                offsets, total_rows, d_in, pl.echunk, epart);
   }
   GPTQ_LAUNCH(channel_energy_reduce_kernel, dim3((d_in + 255) / 256, batch), blk, 0, stream, epart,
-              pl.esplit, d_in, diag_key, n_seen, n_tokens);
+              pl.esplit, d_in, diag_key, n_seen, n_tokens, offsets, total_rows);
   return GPTQ_OK;
 }
 

@@ -24,10 +24,10 @@ _lib = None
 GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_HIP, GPTQ_ERR_WORKSPACE, GPTQ_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 GPTQ_ERR_TOO_LARGE = -6
 NOALLOC_SCRATCH_BYTES = 64 << 20
-WS_HESSIAN, WS_PREPARE, WS_QUANTIZE = 0, 1, 2
+WS_HESSIAN, WS_PREPARE, WS_QUANTIZE, WS_W4A16_REPACK, WS_W4A16 = 0, 1, 2, 3, 4
 
 EXPORTED = ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
-            "gptq_pack_int4",
+            "gptq_accumulate_hessian_grouped", "gptq_pack_int4", "gptq_w4a16_repack", "gptq_w4a16_matmul",
             "gptq_workspace_size", "gptq_status_string", "gptq_version", "gptq_timing_enable", "gptq_timing_read")
 
 
@@ -82,12 +82,15 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(_LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.gptq_accumulate_hessian.argtypes = [i32, i32, i64, i32, vp, i64, i64, vp, i64, vp, vp, vp, sz, vp]
+    L.gptq_accumulate_hessian_grouped.argtypes = [i32, i32, i64, i64, i32, vp, i64, vp, vp, i64, vp, vp, vp, sz, vp]
     L.gptq_prepare_hinv.argtypes = [i32, i32, vp, i64, vp, ctypes.POINTER(_Params), vp, i64, vp, vp, vp, sz, vp]
     L.gptq_quantize_layer.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, vp, vp, ctypes.POINTER(_Params),
                                       vp, vp, vp, vp, vp, sz, vp]
     L.gptq_quantize_layer_noalloc.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, vp, vp,
                                               ctypes.POINTER(_Params), vp, vp, vp, vp, vp]
     L.gptq_pack_int4.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.gptq_w4a16_repack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.gptq_w4a16_matmul.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, i64, vp, sz, vp]
     L.gptq_workspace_size.argtypes = [i32, i32, i32, i32, i64, ctypes.POINTER(_Params)]
     L.gptq_workspace_size.restype = sz
     L.gptq_status_string.argtypes = [i32]
@@ -96,8 +99,9 @@ def lib() -> ctypes.CDLL:
     L.gptq_version.restype = ctypes.c_char_p
     L.gptq_timing_enable.argtypes = [i32]
     L.gptq_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for name in ("gptq_accumulate_hessian", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
-                 "gptq_pack_int4", "gptq_timing_enable", "gptq_timing_read"):
+    for name in ("gptq_accumulate_hessian", "gptq_accumulate_hessian_grouped", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_quantize_layer_noalloc",
+                 "gptq_pack_int4", "gptq_w4a16_repack", "gptq_w4a16_matmul", "gptq_timing_enable",
+                 "gptq_timing_read"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -175,6 +179,54 @@ def accumulate_hessian(X: torch.Tensor, H: torch.Tensor, diag_key: torch.Tensor,
                                          Xb.stride(0) if batch > 1 else n * Xb.stride(1), Hb.data_ptr(),
                                          d_in * d_in, diag_key.data_ptr(), n_seen.data_ptr(), ws.data_ptr(),
                                          ws.numel(), _stream(stream)), "gptq_accumulate_hessian")
+
+
+def accumulate_hessian_grouped(X: torch.Tensor, token_offsets: torch.Tensor, H: torch.Tensor, diag_key: torch.Tensor,
+                               n_seen: torch.Tensor, max_tokens: int, workspace: torch.Tensor | None = None,
+                               stream=None) -> None:
+    """Per-problem token ranges of one buffer: problem e accumulates rows token_offsets[e] ..
+    token_offsets[e + 1] - 1 of token-major X [total, d_in] (at most ``max_tokens`` rows each,
+    the largest count the caller expects); n_seen[e] += the rows it took."""
+    total, d_in = X.shape
+    batch = token_offsets.numel() - 1
+    Hb = _batched(H, 2)
+    if X.dtype not in _DT or H.dtype != torch.float32 or diag_key.dtype != torch.float64 or n_seen.dtype != torch.int64:
+        raise TypeError("X must be fp32/bf16/fp16, H fp32, diag_key fp64, n_seen int64")
+    if token_offsets.dtype != torch.int64 or not token_offsets.is_contiguous() or batch < 1:
+        raise ValueError("token_offsets must be contiguous int64 [batch + 1]")
+    if Hb.shape != (batch, d_in, d_in) or diag_key.numel() != batch * d_in or n_seen.numel() < batch:
+        raise ValueError("shape mismatch between token_offsets, H, diag_key, n_seen")
+    if X.stride(1) != 1 or not Hb.is_contiguous() or not diag_key.is_contiguous():
+        raise ValueError("X rows must be contiguous; H and diag_key contiguous")
+    ws = _workspace(workspace_size(WS_HESSIAN, batch, 0, d_in, max_tokens), X.device, workspace, stream)
+    _check(lib().gptq_accumulate_hessian_grouped(batch, d_in, total, max_tokens, _DT[X.dtype], X.data_ptr(),
+                                                 X.stride(0), token_offsets.data_ptr(), Hb.data_ptr(), d_in * d_in,
+                                                 diag_key.data_ptr(), n_seen.data_ptr(), ws.data_ptr(), ws.numel(),
+                                                 _stream(stream)), "gptq_accumulate_hessian_grouped")
+
+
+class HessianHook:
+    """Calibration hook on a ``torch.nn.Linear`` ("GPTQ Architecture, in depth", "The
+    algorithm in code": a hook records each linear layer's inputs batch by batch): every
+    forward call adds its input, flattened to token-major [tokens, in_features], to H,
+    diag_key and n_seen on the stream the forward runs on.  ``remove()`` detaches it.
+
+    H holds the unnormalised 2 sum x x^T (the running mean of the pages differs by 1/n, and
+    the quantizer's results do not depend on that scale); one H serves every weight that
+    reads the same input (e.g. the q, k and v projections)."""
+
+    def __init__(self, module: torch.nn.Module, in_features: int | None = None, device=None):
+        d_in = in_features if in_features is not None else module.in_features
+        dev = device if device is not None else next(module.parameters()).device
+        self.H, self.diag_key, self.n_seen = new_hessian(d_in, None, dev)
+        self._handle = module.register_forward_pre_hook(self._hook)
+
+    def _hook(self, module, args):
+        x = args[0]
+        accumulate_hessian(x.reshape(-1, x.shape[-1]), self.H, self.diag_key, self.n_seen)
+
+    def remove(self) -> None:
+        self._handle.remove()
 
 
 def prepare_hinv(H: torch.Tensor, diag_key: torch.Tensor, params: Params, workspace: torch.Tensor | None = None,
@@ -279,7 +331,56 @@ def pack_int4(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, st
     return qweight, qzeros, sf16
 
 
-TIME_SYRK, TIME_LAZY_GEMM, TIME_SWEEP, TIME_PACK = 0, 1, 2, 3
+TIME_SYRK, TIME_LAZY_GEMM, TIME_SWEEP, TIME_PACK, TIME_W4A16 = 0, 1, 2, 3, 4
+
+
+def w4a16_repack(qweight: torch.Tensor, g_idx: torch.Tensor, n_groups: int, workspace: torch.Tensor | None = None,
+                 stream=None):
+    """Serving layout of a packed layer: (qweight_s int32 [(b,) d_in/8, d_out], order int32
+    [(b,) d_in]) with the inputs sorted by group.  Raises GptqError on a malformed g_idx."""
+    qb = _batched(qweight, 2)
+    batch, rows8, d_out = qb.shape
+    d_in = rows8 * 8
+    if qweight.dtype != torch.int32 or g_idx.dtype != torch.int32 or g_idx.numel() != batch * d_in:
+        raise TypeError("qweight and g_idx must be int32, g_idx [(b,) d_in]")
+    if not qweight.is_contiguous() or not g_idx.is_contiguous():
+        raise ValueError("qweight and g_idx must be contiguous")
+    qs = torch.empty_like(qweight)
+    order = torch.empty_like(g_idx)
+    _keep_for(stream, qs, order)
+    ws = _workspace(workspace_size(WS_W4A16_REPACK, batch, d_out, d_in), qweight.device, workspace, stream)
+    _check(lib().gptq_w4a16_repack(batch, d_out, d_in, n_groups, qweight.data_ptr(), g_idx.data_ptr(), qs.data_ptr(),
+                                   order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)), "gptq_w4a16_repack")
+    return qs, order
+
+
+def w4a16_matmul(X: torch.Tensor, qweight_s: torch.Tensor, qzeros: torch.Tensor, scales_f16: torch.Tensor,
+                 order: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y fp32 [m, d_out] = X What^T from the packed tensors (X [m, d_in] bf16 / fp16).
+    ``order`` from :func:`w4a16_repack`, or None when qweight is in input order with
+    contiguous groups."""
+    m, d_in = X.shape
+    d_out = qweight_s.shape[-1]
+    n_groups = scales_f16.shape[0]
+    if X.dtype not in (torch.bfloat16, torch.float16) or X.stride(1) != 1:
+        raise TypeError("X must be bf16 or fp16 with contiguous rows")
+    if qweight_s.dtype != torch.int32 or qzeros.dtype != torch.int32 or scales_f16.dtype != torch.float16:
+        raise TypeError("qweight and qzeros int32, scales fp16")
+    if not (qweight_s.is_contiguous() and qzeros.is_contiguous() and scales_f16.is_contiguous()):
+        raise ValueError("packed tensors must be contiguous")
+    if order is not None and (order.dtype != torch.int32 or order.numel() != d_in or not order.is_contiguous()):
+        raise ValueError("order must be contiguous int32 [d_in]")
+    Y = out if out is not None else torch.empty(m, d_out, dtype=torch.float32, device=X.device)
+    if out is None:
+        _keep_for(stream, Y)
+    gsz = -1 if n_groups == 1 else d_in // n_groups
+    ws = _workspace(workspace_size(WS_W4A16, 1, d_out, d_in, m, Params(group_size=gsz)), X.device, workspace, stream)
+    _check(lib().gptq_w4a16_matmul(m, d_out, d_in, n_groups, _DT[X.dtype], X.data_ptr(), X.stride(0),
+                                   qweight_s.data_ptr(), None if order is None else order.data_ptr(), qzeros.data_ptr(),
+                                   scales_f16.data_ptr(), Y.data_ptr(), Y.stride(0), ws.data_ptr(), ws.numel(),
+                                   _stream(stream)), "gptq_w4a16_matmul")
+    return Y
 
 
 def timing_enable(on: bool = True) -> None:

@@ -31,13 +31,13 @@ def test_library_exports_every_declared_symbol():
 
 def test_timing_hook_without_launches():
     gptq.timing_enable(True)
-    for k in (gptq.TIME_SYRK, gptq.TIME_LAZY_GEMM, gptq.TIME_SWEEP, gptq.TIME_PACK):
+    for k in (gptq.TIME_SYRK, gptq.TIME_LAZY_GEMM, gptq.TIME_SWEEP, gptq.TIME_PACK, gptq.TIME_W4A16):
         assert gptq.timing_read(k) == (0.0, 0)
     gptq.timing_enable(False)
     L = gptq.lib()
     assert L.gptq_timing_read(0, None, None) == gptq.GPTQ_ERR_INVALID_ARG
     ms, n = ctypes.c_double(), ctypes.c_int64()
-    assert L.gptq_timing_read(4, ctypes.byref(ms), ctypes.byref(n)) == gptq.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_timing_read(5, ctypes.byref(ms), ctypes.byref(n)) == gptq.GPTQ_ERR_INVALID_ARG
     assert L.gptq_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == gptq.GPTQ_ERR_INVALID_ARG
 
 
@@ -96,6 +96,25 @@ def test_invalid_arguments_are_rejected_before_any_launch():
                                          null) == bad
     assert L.gptq_quantize_layer_noalloc(1, 8192, 8192, 1, 16, 8192, 0, 16, 0, 16, 16, ctypes.byref(p), 16, 16, 16,
                                          16, null) == gptq.GPTQ_ERR_TOO_LARGE
+
+
+def test_w4a16_arguments_are_checked_before_any_launch():
+    L = gptq.lib()
+    bad, unsup = gptq.GPTQ_ERR_INVALID_ARG, gptq.GPTQ_ERR_UNSUPPORTED
+    # matmul: d_out not a multiple of 8, d_in not a multiple of 128, group size 16, fp32 X,
+    # a row stride of Y that is not a multiple of 4, a misaligned Y
+    assert L.gptq_w4a16_matmul(1, 12, 256, 2, 1, 16, 256, 16, None, 16, 16, 16, 12, None, 0, None) == bad
+    assert L.gptq_w4a16_matmul(1, 16, 200, 1, 1, 16, 200, 16, None, 16, 16, 16, 16, None, 0, None) == bad
+    assert L.gptq_w4a16_matmul(1, 16, 256, 16, 1, 16, 256, 16, None, 16, 16, 16, 16, None, 0, None) == unsup
+    assert L.gptq_w4a16_matmul(1, 16, 256, 2, 0, 16, 256, 16, None, 16, 16, 16, 16, None, 0, None) == bad
+    assert L.gptq_w4a16_matmul(1, 16, 256, 2, 1, 16, 256, 16, None, 16, 16, 16, 18, None, 0, None) == bad
+    assert L.gptq_w4a16_matmul(1, 16, 256, 2, 1, 16, 256, 16, None, 16, 16, 24, 16, None, 0, None) == bad
+    # repack: groups that do not divide d_in, a missing workspace
+    assert L.gptq_w4a16_repack(1, 16, 256, 3, 16, 16, 16, 16, 16, 256, None) == bad
+    assert L.gptq_w4a16_repack(1, 16, 256, 2, 16, 16, 16, 16, None, 0, None) == gptq.GPTQ_ERR_WORKSPACE
+    p = gptq.Params(group_size=128)
+    assert gptq.workspace_size(gptq.WS_W4A16, 1, 4096, 14336, 1, p) > 256     # split over K
+    assert gptq.workspace_size(gptq.WS_W4A16, 1, 4096, 14336, 0, p) == 0
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):

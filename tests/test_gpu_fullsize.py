@@ -5,16 +5,10 @@ workload batched in one call per step, default workspaces.
 attn_proj, mlp_up and the MoE experts: the full fp64 oracle (H, U) and a teacher-forced
 replay of sampled rows (rows are independent given U) under the rules of tests/parity.py.
 
-mlp_down (d_in 14336, 262144 tokens): its fp64 Hessian takes ~1e14 flops on the host, so
-H is pinned on sampled blocks (the relative Frobenius error estimated from them) and on
-every fp64 channel energy; the oracle then factors the Hessian made of the GPU's
-off-diagonal entries (pinned by the blocks) and its own fp64 diagonal, and the rules of
-tests/parity.py apply from there on: dead inputs, the ActOrder permutation, U, the
-teacher-forced replay of sampled rows, scales, g_idx and the layer loss.  With
-GPTQ_FULL_ORACLE=1 the oracle accumulates the full fp64 Hessian from X instead.
+mlp_down (d_in 14336, 262144 tokens): the same rules against the full fp64 oracle
+(its Hessian alone is ~1e14 host flops, about a minute on the GPU host's cores), on 64
+sampled rows, after every fp64 channel energy is checked on its own.
 """
-import os
-
 import numpy as np
 import pytest
 
@@ -79,37 +73,12 @@ def test_full_size_mlp_down():
     Ws, Xs = parity.make_inputs(spec)
     parity._progress("inputs ready; GPU layer")
     g = parity.run_gpu(spec, Ws, Xs)
-    parity._progress("GPU layer done; sampled Hessian blocks")
-    X, d = Xs[0], spec.d_in
-    assert int(g["n_seen"].reshape(-1)[0]) == spec.n_tokens
-    Hg = g["H"][0]
-    assert np.array_equal(Hg, Hg.T)
-    # H: a diagonal block and an off-diagonal block of 96 sampled channels each; the
-    # relative Frobenius error is estimated from the sampled entries
-    rng = np.random.default_rng(21)
-    s1 = np.sort(rng.choice(d, 96, replace=False))
-    s2 = np.sort(rng.choice(d, 96, replace=False))
-    num = den = 0.0
-    for a, b in [(s1, s1), (s1, s2)]:
-        Bref = R.ref_hessian_entries(X, spec.dtype, a, b)
-        Bg = Hg[np.ix_(a, b)].astype(np.float64)
-        num += float(np.sum((Bg - Bref) ** 2))
-        den += float(np.sum(Bref ** 2))
-    h_rel = (num / den) ** 0.5
-    assert h_rel <= parity.TOL_H, h_rel
-    # every channel energy (fp64)
+    X = Xs[0]
+    assert np.array_equal(g["H"][0], g["H"][0].T)
     parity._progress("channel energies")
     key = R.ref_channel_energy(X, spec.dtype)
     key_rel = float(np.max(np.abs(g["diag_key"][0] - key) / np.maximum(np.abs(key), 1e-300)))
     assert key_rel <= parity.TOL_KEY, key_rel
-    print("mlp_down", dict(H_rel_fro_sampled=h_rel, key_rel=key_rel), flush=True)
     check_pack(g, 0)
-    rows = sample_rows(spec.d_out, 30, seed=31)
-    if os.environ.get("GPTQ_FULL_ORACLE") == "1":
-        rep = parity.check_problem(spec, Ws[0], X, g, 0, rows=rows)
-    else:
-        H = Hg.astype(np.float64)
-        H[np.diag_indices(d)] = key
-        del g["H"]
-        rep = parity.check_problem(spec, Ws[0], X, g, 0, rows=rows, H=H)
-    print("mlp_down oracle", short(rep), flush=True)
+    rep = parity.check_problem(spec, Ws[0], X, g, 0, rows=sample_rows(spec.d_out, 62, seed=31))
+    print("mlp_down", short(rep), flush=True)
