@@ -49,7 +49,7 @@ def parse():
                     help="weight rows the CPU oracle sweeps (its sweep time is scaled up; rows are independent)")
     ap.add_argument("--cpu-sample-dim", type=int, default=4096,
                     help="leading input channels of the CPU oracle's factorization and sweep (times scaled up)")
-    ap.add_argument("--kernel-timing", choices=("all", "syrk"), default="all",
+    ap.add_argument("--kernel-timing", choices=("all", "syrk"), default="syrk",
                     help="kernel classes bracketed by HIP events inside the timed steps; with 'syrk' the "
                          "other classes are timed over as many extra instrumented steps afterwards")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -162,7 +162,7 @@ def w4a16_decode(gptq, torch, qweight, qzeros, scales_f16, g_idx, n_groups, rows
     for q_, z_, s_ in sets[:2]:
         gptq.w4a16_matmul(X, q_, z_, s_, order, out=Y)
     torch.cuda.synchronize()
-    gptq.timing_enable(True)
+    gptq.timing_enable(True, [gptq.TIME_W4A16])
     gptq.timing_read(gptq.TIME_W4A16)
     for i in range(reps):
         q_, z_, s_ = sets[i % copies]
@@ -262,7 +262,7 @@ def main():
         step(False)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    gptq.timing_enable(True)
+    gptq.timing_enable(True, None if args.kernel_timing == "all" else [gptq.TIME_SYRK])
     read_kernels()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -274,9 +274,7 @@ def main():
     timing_note = "all timed kernel classes bracketed by HIP events inside the timed steps"
     if args.kernel_timing == "syrk":
         # only the SYRK counts from the timed steps; the other classes from as many extra steps
-        for k in ("lazy", "sweep", "pack"):
-            kt[k] = (0.0, 0)
-        gptq.timing_enable(True)
+        gptq.timing_enable(True, [gptq.TIME_LAZY_GEMM, gptq.TIME_SWEEP, gptq.TIME_PACK])
         for _ in range(args.steps):
             step(False)
         torch.cuda.synchronize()

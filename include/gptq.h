@@ -300,8 +300,10 @@ size_t gptq_workspace_size(gptq_ws_call which, int batch, int d_out, int d_in,
  *   GPTQ_TIME_SWEEP      every 128-column sweep kernel of gptq_quantize_layer
  *   GPTQ_TIME_PACK       the packing kernels of one gptq_pack_int4 call (one pair per call)
  *   GPTQ_TIME_W4A16      the kernels of one gptq_w4a16_matmul call (one pair per call)
- * While enabled (on != 0), every such launch is bracketed by a pair of HIP events recorded
- * on the call's stream immediately around it.  gptq_timing_read waits for the recorded
+ * gptq_timing_enable(mask) times the classes whose bit (1 << class) is set in mask (0: none,
+ * -1: all): every launch of such a class is bracketed by a pair of HIP events recorded on
+ * the call's stream immediately around it (each pair adds a few microseconds between
+ * launches, so a class left unset costs nothing).  gptq_timing_read waits for the recorded
  * events of one class, returns their summed elapsed milliseconds and the number of
  * bracketed launches since the previous read of that class, and forgets them.  Events are
  * created by the library on first use and reused; the hook is process-wide and not meant
@@ -314,7 +316,7 @@ typedef enum {
   GPTQ_TIME_PACK = 3,
   GPTQ_TIME_W4A16 = 4
 } gptq_timed_kernel;
-gptq_status gptq_timing_enable(int on);
+gptq_status gptq_timing_enable(int mask);
 gptq_status gptq_timing_read(gptq_timed_kernel which, double* total_ms, int64_t* launches);
 
 /* Static description of a status code. */

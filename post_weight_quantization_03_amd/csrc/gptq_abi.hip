@@ -34,7 +34,7 @@ gptq_status check_params(const gptq_params* p, int d_in, bool need_grid) {
 // reusable events.
 struct TimingState {
   std::mutex mu;
-  bool on = false;
+  int mask = 0;   // bit k: class k is timed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded[gptq::kTimedKinds], pool;
 };
 TimingState& timing() {
@@ -74,7 +74,7 @@ void timing_pair(gptq_timed_kernel kind, hipEvent_t* start, hipEvent_t* stop) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);
   *start = *stop = nullptr;
-  if (!t.on || kind < 0 || kind >= kTimedKinds) return;
+  if (kind < 0 || kind >= kTimedKinds || !(t.mask & (1 << kind))) return;
   std::pair<hipEvent_t, hipEvent_t> p{nullptr, nullptr};
   if (!t.pool.empty()) {
     p = t.pool.back();
@@ -90,10 +90,10 @@ void timing_pair(gptq_timed_kernel kind, hipEvent_t* start, hipEvent_t* stop) {
 
 extern "C" {
 
-gptq_status gptq_timing_enable(int on) {
+gptq_status gptq_timing_enable(int mask) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);
-  t.on = on != 0;
+  t.mask = mask & ((1 << gptq::kTimedKinds) - 1);
   return GPTQ_OK;
 }
 

@@ -44,6 +44,12 @@ constexpr int NBUF = 2;                   // LDS stage buffers per operand
 // operand bytes from LDS but ran slower: one wave per SIMD hides less latency.)
 constexpr int SYRK_WAVES = 8;
 constexpr int kMinTokensPerSplit = 2048;
+// At most this many tokens per slice: the workgroups of a round stream their panels
+// together, and the longer a slice the further apart they drift, so that panels fetched
+// for one are gone from the caches before the others read them (mlp_down SYRK 46.1 ms with
+// 4 slices of 65536 tokens, 45.6 with 8, 44.3 with 16 of 16384; attn_proj's 15 slices of
+// 8738 tokens already fill its rounds).
+constexpr int64_t kMaxTokensPerSplit = 16384;
 
 // Lower tiles (J <= I) of the tile rectangle rows [r0, r1) x columns [c0, c1).
 __device__ __forceinline__ int lower_count(int r0, int r1, int c0, int c1) {
@@ -452,26 +458,32 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   }
 }
 
-// fp32 inputs: 64x64 lower tiles, 256 threads with 4x4 outputs each, FMA in fp32.
+// fp32 inputs: 64x64 lower tiles (blockIdx.x) and token slices (blockIdx.y), 256 threads
+// with 4x4 outputs each, FMA in fp32.  With one slice the tile is added to H directly;
+// otherwise it goes to partial[e][slice][tile][64][64] for syrk_f32_reduce_kernel.
 __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ X, int64_t ldx,
                                                        int64_t bsx, int64_t n_tokens,
                                                        const int64_t* __restrict__ offsets, int64_t total_rows,
-                                                       int d_in, float* __restrict__ H, int64_t bsh) {
+                                                       int d_in, int64_t tokens_per_split, int ntiles,
+                                                       float* __restrict__ partial, float* __restrict__ H,
+                                                       int64_t bsh) {
   __shared__ float sa[16][64];
   __shared__ float sb[16][64];
-  const int e = blockIdx.z;
+  const int e = blockIdx.z, split = blockIdx.y;
   int I, J;
   lower_tile_coords(blockIdx.x, I, J);
   const int I0 = I * 64, J0 = J * 64;
   const Rows pr = problem_rows(offsets, e, n_tokens, total_rows);
+  const int64_t tb = static_cast<int64_t>(split) * tokens_per_split;
+  const int64_t te = min(pr.count, tb + tokens_per_split);
   const float* Xe = X + static_cast<int64_t>(e) * bsx + pr.start * ldx;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4] = {};
-  for (int64_t t0 = 0; t0 < pr.count; t0 += 16) {
+  for (int64_t t0 = tb; t0 < te; t0 += 16) {
     for (int i = threadIdx.x; i < 16 * 64; i += 256) {
       const int k = i >> 6, c = i & 63;
       const int64_t t = t0 + k;
-      const bool okt = t < pr.count;
+      const bool okt = t < te;
       sa[k][c] = (okt && I0 + c < d_in) ? Xe[t * ldx + I0 + c] : 0.0f;
       sb[k][c] = (okt && J0 + c < d_in) ? Xe[t * ldx + J0 + c] : 0.0f;
     }
@@ -491,6 +503,14 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
     }
     __syncthreads();
   }
+  if (gridDim.y > 1) {
+    float* Pt = partial + ((static_cast<int64_t>(e) * gridDim.y + split) * ntiles + blockIdx.x) * 4096;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<float4*>(Pt + (ty * 4 + p) * 64 + tx * 4) = make_float4(acc[p][0], acc[p][1], acc[p][2],
+                                                                              acc[p][3]);
+    return;
+  }
   float* He = H + static_cast<int64_t>(e) * bsh;
   const bool diag = (I == J);
 #pragma unroll
@@ -504,6 +524,31 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
       He[static_cast<int64_t>(row) * d_in + col] += v;
       if (!diag || m > n) He[static_cast<int64_t>(col) * d_in + row] += v;
     }
+}
+
+// Sums the token slices of each 64x64 fp32 tile in slice order and adds twice the sum to H
+// and its mirror (exactly symmetric).  Thread t takes elements t + 256 k of the tile.
+__global__ __launch_bounds__(256) void syrk_f32_reduce_kernel(const float* __restrict__ partial, int nsplit,
+                                                              int ntiles, int d_in, float* __restrict__ H,
+                                                              int64_t bsh) {
+  const int tile = blockIdx.x, e = blockIdx.y;
+  int I, J;
+  lower_tile_coords(tile, I, J);
+  const bool diag = (I == J);
+  float* He = H + static_cast<int64_t>(e) * bsh;
+  const float* P0 = partial + (static_cast<int64_t>(e) * nsplit * ntiles + tile) * 4096;
+  const int64_t kstride = static_cast<int64_t>(ntiles) * 4096;
+#pragma unroll 4
+  for (int k = 0; k < 16; ++k) {
+    const int idx = threadIdx.x + 256 * k, m = idx >> 6, n = idx & 63;
+    float sum = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) sum += P0[sp * kstride + idx];
+    const int row = I * 64 + m, col = J * 64 + n;
+    if (row >= d_in || col >= d_in || (diag && m < n)) continue;
+    const float v = 2.0f * sum;
+    He[static_cast<int64_t>(row) * d_in + col] += v;
+    if (!diag || m > n) He[static_cast<int64_t>(col) * d_in + row] += v;
+  }
 }
 
 // fp64 channel energies sum_t x_tc^2 of one token slice: part[e][slice][c].  A thread
@@ -586,10 +631,11 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
     const int64_t tiles = static_cast<int64_t>(pl.ntiles) * batch;
     const int64_t want = (2048 + tiles - 1) / tiles;
     const int64_t cap = std::max<int64_t>(1, n_tokens / kMinTokensPerSplit);
-    const int64_t base = std::min<int64_t>(std::min(want, cap), 64);
+    const int64_t kmin = std::min<int64_t>((n_tokens + kMaxTokensPerSplit - 1) / kMaxTokensPerSplit, 64);
+    const int64_t base = std::max(kmin, std::min<int64_t>(std::min(want, cap), 64));
     const int n_cu = 256;
     double best = -1.0;
-    for (int64_t k = std::max<int64_t>(1, base - base / 16); k <= 64; ++k) {
+    for (int64_t k = std::max<int64_t>(kmin, std::max<int64_t>(1, base - base / 16)); k <= 64; ++k) {
       int64_t chunk = (n_tokens + k - 1) / k;
       chunk = std::max<int64_t>(SBK, (chunk + SBK - 1) / SBK * SBK);
       if (k > base && chunk < kMinTokensPerSplit) break;
@@ -602,6 +648,15 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
         pl.ksplit = static_cast<int>(std::max<int64_t>(1, ks));
       }
     }
+  }
+  if (!mfma) {
+    // fp32 inputs (small layers): about 512 workgroups over tiles and token slices of at
+    // least 128 tokens, at most 64 slices
+    const int64_t tiles = static_cast<int64_t>(pl.ntiles) * batch;
+    const int64_t k = std::min<int64_t>(std::min<int64_t>((512 + tiles - 1) / tiles, 64),
+                                        std::max<int64_t>(1, n_tokens / 128));
+    pl.kchunk = ((n_tokens + k - 1) / k + 15) / 16 * 16;
+    pl.ksplit = static_cast<int>((n_tokens + pl.kchunk - 1) / pl.kchunk);
   }
   // energy kernel: 16-byte loads of 16 / elem_bytes channels per thread, ~1024 workgroups,
   // at least 256 tokens per slice, at most 256 slices (their sum is one thread per channel)
@@ -623,6 +678,8 @@ size_t plan_bytes(const HessianPlan& pl, int batch, int d_in, float** partial, d
   float* p = nullptr;
   if (pl.mfma)
     p = cv.take<float>(static_cast<size_t>(batch) * pl.ksplit * pl.ntiles * ST * ST);
+  else if (pl.ksplit > 1)
+    p = cv.take<float>(static_cast<size_t>(batch) * pl.ksplit * pl.ntiles * 64 * 64);
   double* q = cv.take<double>(static_cast<size_t>(batch) * pl.esplit * d_in);
   if (partial) *partial = p;
   if (epart) *epart = q;
@@ -700,9 +757,12 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     timing_pair(GPTQ_TIME_SYRK, &ev0, &ev1);
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
-    GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, 1, batch), blk, 0, stream, static_cast<const float*>(X), ldx, bsx,
-                n_tokens, offsets, total_rows, d_in, H, bsh);
+    GPTQ_LAUNCH(syrk_f32_kernel, dim3(pl.ntiles, pl.ksplit, batch), blk, 0, stream, static_cast<const float*>(X), ldx,
+                bsx, n_tokens, offsets, total_rows, d_in, pl.kchunk, pl.ntiles, partial, H, bsh);
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
+    if (pl.ksplit > 1)
+      GPTQ_LAUNCH(syrk_f32_reduce_kernel, dim3(pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
+                  H, bsh);
     GPTQ_LAUNCH(channel_energy_kernel<float>, egrid, blk, 0, stream, static_cast<const float*>(X), ldx, bsx, n_tokens,
                 offsets, total_rows, d_in, pl.echunk, epart);
   }

@@ -37,7 +37,7 @@ constexpr int SV_WAVES = 4;                 // waves per workgroup, side by side
 constexpr int SV_OUT_WAVE = 64;             // outputs per wave: lane group j holds 4 consecutive outputs
 constexpr int SV_OUT = SV_WAVES * SV_OUT_WAVE;
 constexpr int SV_M = 16;                    // activation rows per pass (MFMA rows)
-constexpr int SV_KMAX = 1024;               // largest K chunk staged in LDS
+constexpr int SV_KMAX = 512;                // largest K chunk per workgroup (its weights all in flight)
 constexpr int SV_SEG = 128;                 // fold period of a per-row grid
 
 // ---------------------------------------------------------------------------- repack
@@ -135,22 +135,24 @@ struct ServeArgs {
   int64_t ldy;
 };
 
-// One workgroup: 256 consecutive outputs (64 per wave), one K chunk, 16 activation rows
-// (blockIdx.z selects the pass).  The chunk's activations are gathered into LDS in serving
-// order (rows past m are zero); each 32-input step of a wave loads one 16-byte vector of
-// qweight per lane (4 consecutive outputs of one 8-input row), turns each of its 4 words
-// into the B operand of one MFMA, and adds S through a fifth MFMA against ones.  Lane l
-// owns outputs o0 + 4 (l % 16) + t, t = 0..3; after every SEG inputs (a group, or SEG
-// inputs of a wider group) its partial sums are folded with the scale and zero.  The
-// qweight vectors of the next segment are loaded while the current one is multiplied.
+// One workgroup: 256 consecutive outputs (64 per wave), one K chunk of at most SV_KMAX
+// inputs, 16 activation rows (blockIdx.z selects the pass).  Every lane first issues the
+// loads of all its qweight vectors of the chunk (one 16-byte vector per 32-input step: 4
+// consecutive outputs of one 8-input row), so a wave keeps up to 16 KB of weights in
+// flight; meanwhile the chunk's activations are gathered into LDS in serving order (rows
+// past m are zero).  Each step turns the 4 words of its vector into the B operands of 4
+// MFMAs against the same activations, and a fifth MFMA against ones adds the activation
+// sums.  Lane l owns outputs o0 + 4 (l % 16) + t, t = 0..3; after every SEG inputs (a
+// group, or SEG inputs of a wider group) its sums are folded with the scale and zero.
 template <bool kBF16, int SEG>
 __global__ __launch_bounds__(256) void w4a16_kernel(ServeArgs a) {
   constexpr int LDX = SV_KMAX + 8;   // LDS row pitch (16-bit elements): rows start 16 bytes apart mod 128
   constexpr int NS = SEG / 32;       // 32-input steps per segment
+  constexpr int NSEG = SV_KMAX / SEG;
   __shared__ __attribute__((aligned(16))) uint16_t xs[SV_M * LDX];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = blockIdx.y * a.kchunk;
-  const int kn = min(a.kchunk, a.d_in - k0);
+  const int kn = min(a.kchunk, a.d_in - k0);   // a multiple of SEG
   const int m0 = blockIdx.z * SV_M;
 
   const int o0 = blockIdx.x * SV_OUT + wave * SV_OUT_WAVE;
@@ -160,57 +162,66 @@ __global__ __launch_bounds__(256) void w4a16_kernel(ServeArgs a) {
   const int obc = live ? ob : 0;
   const uint4* qw = reinterpret_cast<const uint4*>(a.qweight + obc);
   const int64_t row4 = a.d_out / 4;           // uint4 per qweight row
-  // inputs k0 + s0 + 32 t + 8 q .. + 7 of step t sit in qweight row (k0 + s0) / 8 + 4 t + q
-  auto load_seg = [&](int s0, uint4* w) {
+  // step i covers inputs k0 + 32 i + 8 q .. + 7: qweight row k0 / 8 + 4 i + q
+  uint4 w[NSEG * NS];
 #pragma unroll
-    for (int t = 0; t < NS; ++t) w[t] = qw[static_cast<int64_t>((k0 + s0) / 8 + 4 * t + q) * row4];
-  };
-  uint4 cur[NS], nxt[NS];
-  load_seg(0, cur);   // in flight while the activations are staged
-
-  // stage the activations: element (r, k) = X[m0 + r][order[k0 + k]], zero past m
-  for (int i = tid; i < SV_M * kn; i += 256) {
-    const int r = i / kn, k = i - r * kn;
-    uint16_t v = 0;
-    if (m0 + r < a.m) {
-      const int c = a.order ? min(max(a.order[k0 + k], 0), a.d_in - 1) : k0 + k;
-      v = a.X[static_cast<int64_t>(m0 + r) * a.ldx + c];
+  for (int i = 0; i < NSEG * NS; ++i)
+    if (32 * i < kn) w[i] = qw[static_cast<int64_t>(k0 / 8 + 4 * i + q) * row4];
+  // the scales (4 fp16) and zeros (one qzeros word) of every segment's group, also up front
+  uint2 sv[NSEG];
+  uint32_t zw[NSEG];
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    if (sg * SEG < kn) {
+      const int g = (k0 + sg * SEG) / a.gs;
+      sv[sg] = *reinterpret_cast<const uint2*>(a.scales + static_cast<int64_t>(g) * a.d_out + obc);
+      zw[sg] = static_cast<uint32_t>(a.qzeros[static_cast<int64_t>(g) * (a.d_out / 8) + obc / 8]);
     }
-    xs[r * LDX + k] = v;
   }
+
+  // stage the activations: element (r, k) = X[m0 + r][order[k0 + k]], zero past m; the
+  // gather's index loads of a thread are independent of each other (unrolled)
+  const int mrows = min(SV_M, a.m - m0);
+#pragma unroll 4
+  for (int i = tid; i < mrows * kn; i += 256) {
+    const int r = i / kn, k = i - r * kn;
+    const int c = a.order ? min(max(a.order[k0 + k], 0), a.d_in - 1) : k0 + k;
+    xs[r * LDX + k] = a.X[static_cast<int64_t>(m0 + r) * a.ldx + c];
+  }
+  for (int i = tid; i < (SV_M - mrows) * (LDX / 8); i += 256)
+    reinterpret_cast<uint4*>(xs + mrows * LDX)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
   const s16x8 ones = kBF16 ? s16x8{0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80}
                            : s16x8{0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00};
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   f32x4 y[4] = {zero4, zero4, zero4, zero4};
-  for (int s0 = 0; s0 < kn; s0 += SEG) {
-    if (s0 + SEG < kn) load_seg(s0 + SEG, nxt);
-    f32x4 acc[4] = {zero4, zero4, zero4, zero4};
-    f32x4 sacc = zero4;
 #pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const s16x8 av = *reinterpret_cast<const s16x8*>(xs + j * LDX + s0 + 32 * t + 8 * q);
-      acc[0] = mma16<kBF16>(av, codes16<kBF16>(cur[t].x), acc[0]);
-      acc[1] = mma16<kBF16>(av, codes16<kBF16>(cur[t].y), acc[1]);
-      acc[2] = mma16<kBF16>(av, codes16<kBF16>(cur[t].z), acc[2]);
-      acc[3] = mma16<kBF16>(av, codes16<kBF16>(cur[t].w), acc[3]);
-      sacc = mma16<kBF16>(av, ones, sacc);
+  for (int sg = 0; sg < NSEG; ++sg) {
+    const int s0 = sg * SEG;
+    if (s0 < kn) {
+      f32x4 acc[4] = {zero4, zero4, zero4, zero4};
+      f32x4 sacc = zero4;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const uint4 wv = w[sg * NS + t];
+        const s16x8 av = *reinterpret_cast<const s16x8*>(xs + j * LDX + s0 + 32 * t + 8 * q);
+        acc[0] = mma16<kBF16>(av, codes16<kBF16>(wv.x), acc[0]);
+        acc[1] = mma16<kBF16>(av, codes16<kBF16>(wv.y), acc[1]);
+        acc[2] = mma16<kBF16>(av, codes16<kBF16>(wv.z), acc[2]);
+        acc[3] = mma16<kBF16>(av, codes16<kBF16>(wv.w), acc[3]);
+        sacc = mma16<kBF16>(av, ones, sacc);
+      }
+      // fold with the segment's group: the lane's 4 outputs share one qzeros word
+      const uint32_t sh[2] = {sv[sg].x, sv[sg].y};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sh[t / 2] >> (16 * (t & 1)))));
+        const float z = static_cast<float>((zw[sg] >> (4 * ((obc % 8) + t))) & 15u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[t][r] = fmaf(s, fmaf(-z, sacc[r], acc[t][r]), y[t][r]);
+      }
     }
-    // fold: group of this segment; the lane's 4 outputs share one qzeros word
-    const int g = (k0 + s0) / a.gs;
-    const uint2 sv = *reinterpret_cast<const uint2*>(a.scales + static_cast<int64_t>(g) * a.d_out + obc);
-    const uint32_t zw = static_cast<uint32_t>(a.qzeros[static_cast<int64_t>(g) * (a.d_out / 8) + obc / 8]);
-    const uint32_t sh[2] = {sv.x, sv.y};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sh[t / 2] >> (16 * (t & 1)))));
-      const float z = static_cast<float>((zw >> (4 * ((obc % 8) + t))) & 15u);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[t][r] = fmaf(s, fmaf(-z, sacc[r], acc[t][r]), y[t][r]);
-    }
-#pragma unroll
-    for (int t = 0; t < NS; ++t) cur[t] = nxt[t];
   }
   if (!live) return;
   // lane holds rows 4 q + r of the pass, outputs ob .. ob + 3
@@ -226,13 +237,22 @@ __global__ __launch_bounds__(256) void w4a16_kernel(ServeArgs a) {
 
 __global__ void clear_flag_kernel(int* __restrict__ flag) { *flag = 0; }
 
-// Y[m][o] = sum over chunks of the partials, in chunk order.
+// Y[m][o] = sum over chunks of the partials, in chunk order.  The loads of 8 chunks are
+// issued together before they are added (one load after another would put every load's
+// latency on the chain).
 __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float* __restrict__ part, int chunks, int m,
                                                            int d_out, float* __restrict__ Y, int64_t ldy) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<int64_t>(m) * d_out) return;
+  const int64_t n = static_cast<int64_t>(m) * d_out;
+  if (i >= n) return;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += part[static_cast<int64_t>(c) * m * d_out + i];
+  for (int c0 = 0; c0 < chunks; c0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = c0 + c < chunks ? part[static_cast<int64_t>(c0 + c) * n + i] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += v[c];
+  }
   const int64_t r = i / d_out, o = i - r * d_out;
   Y[r * ldy + o] = s;
 }

@@ -383,10 +383,13 @@ def w4a16_matmul(X: torch.Tensor, qweight_s: torch.Tensor, qzeros: torch.Tensor,
     return Y
 
 
-def timing_enable(on: bool = True) -> None:
-    """Start/stop recording HIP events around every timed kernel launch (SYRK, lazy-update
-    products, column sweeps, packing)."""
-    _check(lib().gptq_timing_enable(int(on)), "gptq_timing_enable")
+def timing_enable(on: bool = True, kinds=None) -> None:
+    """Start/stop recording HIP events around the launches of the timed kernel classes
+    (``kinds``: an iterable of TIME_* values, all of them when None)."""
+    mask = 0
+    if on:
+        mask = -1 if kinds is None else sum(1 << k for k in set(kinds))
+    _check(lib().gptq_timing_enable(mask), "gptq_timing_enable")
 
 
 def timing_read(which: int = TIME_SYRK):
