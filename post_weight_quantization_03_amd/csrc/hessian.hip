@@ -207,16 +207,19 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][SBK * ST];
   __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][SBK * ST];
 
-  // (slice, tile) of this workgroup.  Workgroups start in linear order, dealt to the 8
-  // XCDs round-robin (XCD = id % 8), one per CU, so the running ones form a window of about
-  // 256 consecutive ids.  Positions are slice-major; inside each full run of 256 ids, the
-  // workgroup dealt to XCD x in slot s takes position 32 x + s, so every XCD works on 32
-  // consecutive positions (one sub-block of round_tile_coords) of the same token slice.
-  const int e = blockIdx.y;
+  // (problem, slice, tile) of this workgroup.  Workgroups start in linear order over the
+  // whole grid (x fastest), dealt to the 8 XCDs round-robin (XCD = id % 8), one per CU, so
+  // the running ones form a window of about 256 consecutive ids.  Positions are problem-
+  // then slice-major; inside each full run of 256 ids, the workgroup dealt to XCD x in slot
+  // s takes position 32 x + s, so every XCD works on 32 consecutive positions (one sub-block
+  // of round_tile_coords) of the same problem and token slice.
   const int total = ntiles * ksplit;
-  const int lin = blockIdx.x;
+  const int all = total * static_cast<int>(gridDim.y);
+  const int lin = static_cast<int>(blockIdx.y) * total + static_cast<int>(blockIdx.x);
   const int rnd = lin >> 8, p = lin & 255;
-  const int idx = (rnd + 1) * 256 <= total ? (rnd << 8) + 32 * (p & 7) + (p >> 3) : lin;
+  const int gidx = (rnd + 1) * 256 <= all ? (rnd << 8) + 32 * (p & 7) + (p >> 3) : lin;
+  const int e = gidx / total;
+  const int idx = gidx - e * total;
   const int split = idx / ntiles;
   const int tile = idx - split * ntiles;
   int I, J;
