@@ -286,26 +286,41 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
   float w[C];
 #pragma unroll
   for (int m = 0; m < C; ++m) w[m] = wrow[LPR * m + k];
-  // stage the U block: thread (row j, lane kk) gathers U[j][LPR m + kk], m = 0..C-1 (each
+  // stage the U block: item i = (row j, lane kk) gathers U[j][LPR m + kk], m = 0..C-1 (each
   // load instruction reads LPR consecutive floats per row) and writes them as C
-  // consecutive floats
-#pragma unroll 1
-  for (int i = tid; i < kBlock * LPR; i += NT) {
-    const int j = i / LPR, kk = i % LPR;
-    const float* src = Ub + static_cast<int64_t>(j) * d_in + kk;
-    float v[C];
+  // consecutive floats.  A thread's items are all loaded before any is stored, so their
+  // loads overlap (one item at a time left the block's 64 KB as SI serial load latencies).
+  constexpr int ITEMS = kBlock * LPR;
+  constexpr int SI = (ITEMS + NT - 1) / NT;   // items per thread
+  {
+    float v[SI][C];
 #pragma unroll
-    for (int m = 0; m < C; ++m) v[m] = src[LPR * m];
+    for (int s = 0; s < SI; ++s) {
+      const int i = tid + s * NT;
+      if (ITEMS % NT == 0 || i < ITEMS) {
+        const float* src = Ub + static_cast<int64_t>(i / LPR) * d_in + i % LPR;
 #pragma unroll
-    for (int m = 0; m < C; ++m) {
-      if (LPR * m + kk == j) {
-        inv_d[j] = 1.0f / v[m];
-        v[m] = 0.0f;
+        for (int m = 0; m < C; ++m) v[s][m] = src[LPR * m];
       }
     }
-    float4* dst = reinterpret_cast<float4*>(Ul + j * UR + CP * kk);
 #pragma unroll
-    for (int q = 0; q < CQ; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    for (int s = 0; s < SI; ++s) {
+      const int i = tid + s * NT;
+      if (ITEMS % NT == 0 || i < ITEMS) {
+        const int j = i / LPR, kk = i % LPR;
+#pragma unroll
+        for (int m = 0; m < C; ++m) {
+          if (LPR * m + kk == j) {
+            inv_d[j] = 1.0f / v[s][m];
+            v[s][m] = 0.0f;
+          }
+        }
+        float4* dst = reinterpret_cast<float4*>(Ul + j * UR + CP * kk);
+#pragma unroll
+        for (int q = 0; q < CQ; ++q)
+          dst[q] = make_float4(v[s][4 * q], v[s][4 * q + 1], v[s][4 * q + 2], v[s][4 * q + 3]);
+      }
+    }
   }
   __syncthreads();
   if (!live) return;   // whole rows leave together; no barrier follows
