@@ -5,6 +5,8 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
+#include <utility>
 
 #include "gptq.h"
 
@@ -28,6 +30,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 128;  // columns per lazy batch
+
+// f(std::integral_constant<int, I>) for every I of the sequence, in order (a loop whose
+// index is a compile-time constant in its body)
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

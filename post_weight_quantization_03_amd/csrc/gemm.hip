@@ -285,6 +285,14 @@ __device__ __forceinline__ void split3(const float4 v, uint2& p0, uint2& p1, uin
   p2 = make_uint2(a2, b2);
 }
 
+// v where `in`, else zeros, as bitwise ANDs (a select here compiles to a branch, which
+// would split the loop body into blocks that the scheduler cannot interleave)
+__device__ __forceinline__ float4 masked(const float4 v, bool in) {
+  const uint32_t k = in ? 0xFFFFFFFFu : 0u;
+  return make_float4(__uint_as_float(__float_as_uint(v.x) & k), __uint_as_float(__float_as_uint(v.y) & k),
+                     __uint_as_float(__float_as_uint(v.z) & k), __uint_as_float(__float_as_uint(v.w) & k));
+}
+
 template <bool kTransB, int kRole>
 __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   constexpr int GT = 128, GK = 16;
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
     for (int q = 0; q < RQ; ++q) {
       const int f = tid + 256 * q;
       const bool in = (r0 + f / 4 < rlim) && (k0 + 4 * (f % 4) < ke);
-      const float4 v = in ? r[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = masked(r[q], in);
       uint2 p0, p1, p2;
       split3(v, p0, p1, p2);
       const int row = f / 4, k4 = f % 4;
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
     for (int q = 0; q < RQ; ++q) {
       const int f = tid + 256 * q;
       const bool in = (k0 + f / (GT / 4) < ke) && (n0 + 4 * (f % (GT / 4)) < g.N);
-      const float4 v = in ? r[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = masked(r[q], in);
       uint2 p0, p1, p2;
       split3(v, p0, p1, p2);
       const int k = f / (GT / 4);
@@ -460,6 +468,17 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
                                                                   __builtin_bit_cast(bf16x8, bv[PJ[t]][bn]),
                                                                   acc[bm][bn], 0, 0, 0);
       store_stage(s + 1, buf ^ 1, buf ^ 1);   // past the last stage: zeros, never read
+      // The next stage's split (VALU) and LDS stores are independent of this stage's
+      // products: interleave them, a few instructions after every MFMA, so that the matrix
+      // core keeps issuing while they run (left to itself the scheduler issues all MFMAs
+      // first, and the waves of a workgroup, in step between barriers, then all split at
+      // once with the matrix core idle).
+      static_for(std::make_integer_sequence<int, 24>{}, [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+        if constexpr (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // an LDS store
+      });
       __syncthreads();
     };
     for (int s = 0; s < nk2; s += 2) {

@@ -438,16 +438,28 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
       acc[q].x += v.x; acc[q].y += v.y; acc[q].z += v.z; acc[q].w += v.w;
     }
   }
+  // the four columns of a thread's row are added with one 16-byte read-modify-write where
+  // all four are inside H and on or below the diagonal (and H's rows are 16-byte aligned)
+  const bool vec_rows = (d_in % 4 == 0) && (reinterpret_cast<uintptr_t>(He) % 16 == 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int i = r0 + 16 * q, m = sm + i;
     const float v[4] = {2.0f * acc[q].x, 2.0f * acc[q].y, 2.0f * acc[q].z, 2.0f * acc[q].w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = sn + c4 + t;
-      tr[i][c4 + t] = v[t];
-      const int row = I * ST + m, col = J * ST + n;
-      if (row < d_in && col < d_in && (!diag || m >= n)) He[static_cast<int64_t>(row) * d_in + col] += v[t];
+    for (int t = 0; t < 4; ++t) tr[i][c4 + t] = v[t];
+    const int row = I * ST + m, col0 = J * ST + sn + c4;
+    if (vec_rows && row < d_in && col0 + 3 < d_in && (!diag || m >= sn + c4 + 3)) {
+      float4* h = reinterpret_cast<float4*>(He + static_cast<int64_t>(row) * d_in + col0);
+      float4 o = *h;
+      o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
+      *h = o;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = sn + c4 + t;
+        const int col = col0 + t;
+        if (row < d_in && col < d_in && (!diag || m >= n)) He[static_cast<int64_t>(row) * d_in + col] += v[t];
+      }
     }
   }
   __syncthreads();

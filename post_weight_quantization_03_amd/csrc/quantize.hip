@@ -234,11 +234,6 @@ __device__ __forceinline__ float grp_max(float v) {
   }
 }
 
-template <int... I, typename F>
-__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-
 // One 128-column block of the sweep.  G = group size (16, 32, 64 or 128), or 0 for the
 // per-row grid already written by row_grid_kernel.  kStatic (with G = 0): every column
 // takes the grid of its original group, perm[column] / gsz, written before the sweep by
