@@ -341,10 +341,17 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
     z = static_cast<float>(zr[r]);
     inv_s = 1.0f / s;
   }
-  // lane k stores the codes of columns C k .. C k + C - 1
-  uint32_t cw[CW];
+  // Codes.  16 lanes per row: the owner of a column keeps its code, as it keeps its error,
+  // and each lane stores the codes of its own columns.  4 lanes per row: lane k packs the
+  // codes of columns C k .. C k + C - 1 (every lane has every code).
+  constexpr bool kOwnCodes = LPR == 16;
+  float qv[kOwnCodes ? C : 1];
+  uint32_t cw[kOwnCodes ? 1 : CW];
+  if constexpr (!kOwnCodes) {
 #pragma unroll
-  for (int q = 0; q < CW; ++q) cw[q] = 0u;
+    for (int q = 0; q < CW; ++q) cw[q] = 0u;
+  }
+  float zmax = maxq - z;   // upper clamp of code - zero for the current group
   const float* ul_k = Ul + CP * k;
   // U row j is read into registers one column ahead (two alternating sets), so that the
   // LDS latency stays off the column-to-column chain
@@ -381,6 +388,7 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
       hi = grp_max<LPR>(hi);
       fit_grid(lo, hi, maxq, sym != 0, s, z);
       inv_s = 1.0f / s;
+      zmax = maxq - z;
       if (k == 0) {
         const int gi = (j0 + j) / G;
         sc[static_cast<int64_t>(gi) * d_out + r] = s;
@@ -393,10 +401,18 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
       z = grp_bcast<LPR, j % LPR>(g_z[mj]);
     }
     const float wj = grp_bcast<LPR, j % LPR>(w[mj]);
-    const float q = fminf(fmaxf(rintf(wj * inv_s) + z, 0.0f), maxq);
-    const float wq = s * (q - z);
-    const float e_j = (wj - wq) * dj;
-    cw[(j % C) / 4] |= (k == j / C) ? (static_cast<uint32_t>(q) << (8 * (j & 3))) : 0u;
+    // t = code - zero: round(w / s) clamped to [-z, maxq - z] (the code clamp(round(w / s)
+    // + z, 0, maxq) less z, exactly), so that the dequantized value is s t and the scaled
+    // error (w - s t) / U_jj takes one fused multiply-add and a multiply
+    const float zq = kStatic ? maxq - z : zmax;
+    const float t = __builtin_amdgcn_fmed3f(rintf(wj * inv_s), -z, zq);
+    const float e_j = fmaf(-s, t, wj) * dj;
+    const float q = t + z;
+    if constexpr (kOwnCodes) {
+      if (k == j % LPR) qv[mj] = q;   // the owner keeps the code of its column
+    } else {
+      cw[(j % C) / 4] |= (k == j / C) ? (static_cast<uint32_t>(q) << (8 * (j & 3))) : 0u;
+    }
 #pragma unroll
     for (int m = mj; m < C; ++m) {
       const float4 u4 = cur[m / 4];
@@ -405,10 +421,12 @@ __global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict
     }
     if (k == j % LPR) w[mj] = e_j;   // the owner keeps err_j in place of w_j
   });
-  uint32_t* cdst = reinterpret_cast<uint32_t*>(codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0 + C * k);
-  if constexpr (CW == 2) {
-    *reinterpret_cast<uint2*>(cdst) = make_uint2(cw[0], cw[1]);
+  uint8_t* crow = codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
+  if constexpr (kOwnCodes) {
+#pragma unroll
+    for (int m = 0; m < C; ++m) crow[LPR * m + k] = static_cast<uint8_t>(qv[m]);
   } else {
+    uint32_t* cdst = reinterpret_cast<uint32_t*>(crow + C * k);
 #pragma unroll
     for (int q = 0; q < CW; q += 4) *reinterpret_cast<uint4*>(cdst + q) = make_uint4(cw[q], cw[q + 1], cw[q + 2], cw[q + 3]);
   }
