@@ -18,9 +18,9 @@
 //
 // The fp64 diagonal key 2 * sum_t x^2 (exact products, fp64 sums) decides the ActOrder
 // permutation, where fp32 sums are not precise enough to order nearly equal channels
-// reproducibly.  A separate memory-bound kernel accumulates it (for 16-bit inputs on the
-// side stream, after the SYRK and next to its reduction); per-slice fp64 partials are
-// summed in a fixed order.
+// reproducibly.  For 16-bit inputs the SYRK's diagonal tiles add it up from the tokens
+// they already hold in LDS (X is read once); for fp32 inputs a separate memory-bound kernel
+// does.  Per-slice fp64 partials are summed in a fixed order.
 #include <algorithm>
 
 #include "common.h"
@@ -203,7 +203,8 @@ __device__ __forceinline__ int chunk_logical(int t, int p) {
 template <bool kF16, int NW>
 __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t bsx, int64_t n_tokens, const int64_t* __restrict__ offsets,
-    int64_t total_rows, int d_in, int64_t tokens_per_split, int ksplit, float* __restrict__ partial, int ntiles) {
+    int64_t total_rows, int d_in, int64_t tokens_per_split, int ksplit, float* __restrict__ partial, int ntiles,
+    double* __restrict__ epart) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[NBUF][SBK * ST];
   __shared__ __attribute__((aligned(16))) uint16_t sB[NBUF][SBK * ST];
 
@@ -318,6 +319,30 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(reinterpret_cast<const char*>(stage) + byte));
   };
 
+  // fp64 channel energies, on diagonal tiles only (each token slice of each channel passes
+  // through exactly one of them): thread (cg = tid % 64, tg = tid / 64) adds the squares of
+  // channels I0 + 4 cg .. + 3 over tokens 8 tg .. 8 tg + 7 of every stage, in token order
+  // (squares of 16-bit values are exact in fp64).
+  static_assert(NW == 8 && SBK == 64, "energy thread map: 64 channel quads x 8 token octets");
+  const int e_cg = tid & 63, e_tg = tid >> 6;
+  double en[4] = {0.0, 0.0, 0.0, 0.0};
+  auto energies = [&](int stage) {
+    const char* base = reinterpret_cast<const char*>(sA[stage % NBUF]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 8 * e_tg + i;
+      const uint2 raw =
+          *reinterpret_cast<const uint2*>(base + t * (2 * ST) + 16 * chunk_phys(t, e_cg >> 1) + 8 * (e_cg & 1));
+      const uint32_t hw[4] = {raw.x & 0xFFFFu, raw.x >> 16, raw.y & 0xFFFFu, raw.y >> 16};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double x = static_cast<double>(kF16 ? f16_to_f32(static_cast<uint16_t>(hw[c]))
+                                                  : bf16_to_f32(static_cast<uint16_t>(hw[c])));
+        en[c] = fma(x, x, en[c]);
+      }
+    }
+  };
+
   // Copies in flight per wave per stage (the fast path; tail stages load through
   // registers and are complete when issued).  Waiting for a stage means allowing the
   // copies of the `later` stages issued after it to stay outstanding.
@@ -379,6 +404,7 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
   for (int s = 0; s < nstages; ++s) {
     read_ops(s, 1, Q);
     mma(P);
+    if (diag) energies(s);
     read_ops(s, 2, P);
     mma(Q);
     read_ops(s, 3, Q);
@@ -403,6 +429,21 @@ __global__ __launch_bounds__(64 * NW) void syrk_mfma_kernel(
         const int n = WC * wn + 32 * bn + (lane & 31);
         Pt[m * ST + n] = acc[bm][bn][r];
       }
+  if (diag) {
+    // the 8 token octets of each channel summed in order through LDS (free after the loop),
+    // then this slice's energies of the tile's channels to epart[e][split][channel]
+    __syncthreads();
+    double* red = reinterpret_cast<double*>(&sA[0][0]);   // [8][256]
+#pragma unroll
+    for (int c = 0; c < 4; ++c) red[e_tg * ST + 4 * e_cg + c] = en[c];
+    __syncthreads();
+    if (tid < ST && I0 + tid < d_in) {
+      double sum = 0.0;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) sum += red[g * ST + tid];
+      epart[(static_cast<int64_t>(e) * ksplit + split) * d_in + I0 + tid] = sum;
+    }
+  }
 }
 
 // Sums the token-slice partials of each lower tile in slice order and adds twice the
@@ -673,6 +714,11 @@ HessianPlan make_plan(int batch, int d_in, int64_t n_tokens, bool mfma) {
     pl.kchunk = ((n_tokens + k - 1) / k + 15) / 16 * 16;
     pl.ksplit = static_cast<int>((n_tokens + pl.kchunk - 1) / pl.kchunk);
   }
+  if (mfma) {   // energies from the SYRK's diagonal tiles, one partial per token slice
+    pl.esplit = pl.ksplit;
+    pl.echunk = pl.kchunk;
+    return pl;
+  }
   // energy kernel: 16-byte loads of 16 / elem_bytes channels per thread, ~1024 workgroups,
   // at least 256 tokens per slice, at most 256 slices (their sum is one thread per channel)
   const int vec = mfma ? 8 : 4;
@@ -726,17 +772,8 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
   plan_bytes(pl, batch, d_in, &partial, &epart, ws);
 
   const dim3 blk(256);
-  const dim3 egrid((d_in + 256 * (mfma ? 8 : 4) - 1) / (256 * (mfma ? 8 : 4)), pl.esplit, batch);
   if (mfma) {
-    // The fp64 channel energies (memory-bound) run on the side stream once the SYRK is done,
-    // next to the partial-tile reduction; the main stream joins them before the energy
-    // reduction.  Run concurrently with the SYRK, their reads of X slowed it by more than
-    // they cost alone (mlp_down: Hessian 54.4 -> 53.1 ms when run after it).
-    std::lock_guard<std::mutex> lk(side_mutex());
-    SideStream* ss = nullptr;
-    if (const gptq_status st = side_stream(&ss); st != GPTQ_OK) return st;
-
-
+    // The fp64 channel energies come out of the SYRK's diagonal tiles (epart[e][slice][c]).
     const dim3 sblk(64 * SYRK_WAVES);
     const dim3 grid(pl.ntiles * pl.ksplit, batch);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
@@ -749,25 +786,14 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
     if (x_dtype == GPTQ_F16) {
       GPTQ_LAUNCH((syrk_mfma_kernel<true, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, offsets,
-                  total_rows, d_in, pl.kchunk, pl.ksplit, partial, pl.ntiles);
+                  total_rows, d_in, pl.kchunk, pl.ksplit, partial, pl.ntiles, epart);
     } else {
       GPTQ_LAUNCH((syrk_mfma_kernel<false, SYRK_WAVES>), grid, sblk, 0, stream, Xh, ldx, bsx, n_tokens, offsets,
-                  total_rows, d_in, pl.kchunk, pl.ksplit, partial, pl.ntiles);
+                  total_rows, d_in, pl.kchunk, pl.ksplit, partial, pl.ntiles, epart);
     }
     if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
-    GPTQ_HIP_TRY(hipEventRecord(ss->fork, stream));
-    GPTQ_HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
-    if (x_dtype == GPTQ_F16) {
-      GPTQ_LAUNCH(channel_energy_kernel<F16>, egrid, blk, 0, ss->s, static_cast<const F16*>(X), ldx, bsx, n_tokens,
-                  offsets, total_rows, d_in, pl.echunk, epart);
-    } else {
-      GPTQ_LAUNCH(channel_energy_kernel<BF16>, egrid, blk, 0, ss->s, static_cast<const BF16*>(X), ldx, bsx,
-                  n_tokens, offsets, total_rows, d_in, pl.echunk, epart);
-    }
-    GPTQ_HIP_TRY(hipEventRecord(ss->join, ss->s));
     GPTQ_LAUNCH(syrk_reduce_kernel, dim3(16, pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
                 H, bsh);
-    GPTQ_HIP_TRY(hipStreamWaitEvent(stream, ss->join, 0));
   } else {
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     timing_pair(GPTQ_TIME_SYRK, &ev0, &ev1);
@@ -778,6 +804,7 @@ gptq_status hessian_enqueue(int batch, int d_in, int64_t n_tokens, gptq_dtype x_
     if (pl.ksplit > 1)
       GPTQ_LAUNCH(syrk_f32_reduce_kernel, dim3(pl.ntiles, batch), blk, 0, stream, partial, pl.ksplit, pl.ntiles, d_in,
                   H, bsh);
+    const dim3 egrid((d_in + 1023) / 1024, pl.esplit, batch);
     GPTQ_LAUNCH(channel_energy_kernel<float>, egrid, blk, 0, stream, static_cast<const float*>(X), ldx, bsx, n_tokens,
                 offsets, total_rows, d_in, pl.echunk, epart);
   }
