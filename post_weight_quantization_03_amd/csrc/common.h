@@ -148,6 +148,10 @@ struct GemmArgs {
   int batch2 = 1;
   int64_t sA2 = 0, sB2 = 0, sC2 = 0;
   int role = 0;                      // 1: a lazy trailing update of the quantizer (see gemm.hip)
+  // > 0: a product that runs next to a latency-bound chain on another stream; it is given
+  // at most this many CUs, one workgroup each (see gemm.hip), so that the chain's kernels
+  // find free CUs
+  int max_cus = 0;
 };
 enum GemmFlags {
   kLowerOut = 1,   // C square: only tiles on or below the diagonal are computed

@@ -17,6 +17,7 @@
 // Both: 256 threads = 4 waves, each owning a quarter of the tile as 32 x 32 MFMA blocks;
 // triangular operands shrink the K range per tile; a lower-only output skips tiles above
 // the diagonal.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -293,18 +294,18 @@ __device__ __forceinline__ float4 masked(const float4 v, bool in) {
                      __uint_as_float(__float_as_uint(v.z) & k), __uint_as_float(__float_as_uint(v.w) & k));
 }
 
-template <bool kTransB, int kRole>
-__global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
+// One 128 x 128 tile (column tile bx, row tile by, product bz) of the split-bf16 product.
+template <bool kTransB>
+__device__ __forceinline__ void gemm_x6_tile(const GemmArgs& g, int bx, int by, int bz) {
   constexpr int GT = 128, GK = 16;
   constexpr int PA = GK;                       // bf16 per K-contiguous row (two 16-byte chunks)
   constexpr int PB = GT;                       // bf16 per k row of the N-contiguous layout
   constexpr int A_PLANE = GT * PA;
   constexpr int B_PLANE = kTransB ? GT * PA : GK * PB;
   constexpr int RQ = GT * GK / 1024;           // float4 per thread per operand and stage (2)
-  const int bx = static_cast<int>((blockIdx.x + blockIdx.y + blockIdx.z) % gridDim.x);
-  const int n0 = bx * GT, m0 = blockIdx.y * GT;
+  const int n0 = bx * GT, m0 = by * GT;
   if ((g.flags & kLowerOut) && n0 > m0) return;
-  const int zo = blockIdx.z / g.batch2, zi = blockIdx.z % g.batch2;
+  const int zo = bz / g.batch2, zi = bz % g.batch2;
   const float* A = g.A + static_cast<int64_t>(zo) * g.sA + static_cast<int64_t>(zi) * g.sA2;
   const float* B = g.B + static_cast<int64_t>(zo) * g.sB + static_cast<int64_t>(zi) * g.sB2;
   float* C = g.C + static_cast<int64_t>(zo) * g.sC + static_cast<int64_t>(zi) * g.sC2;
@@ -511,7 +512,44 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
     }
 }
 
+// kPersist: a grid of fewer workgroups than tiles, each taking every gridDim.x-th tile in
+// turn (lower tiles only with kLowerOut, row by row); otherwise one tile per workgroup
+// (column index rotated by the row and batch index: workgroups are dealt to the 8 XCDs
+// round-robin by linear id, and with triangular operands or a lower-only output the work
+// of a tile depends on its column).
+template <bool kTransB, int kRole, bool kPersist = false>
+__global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
+  if constexpr (kPersist) {
+    const int tm = (g.M + 127) / 128, tn = (g.N + 127) / 128;
+    const bool lower = (g.flags & kLowerOut) != 0;
+    const int per = lower ? tm * (tm + 1) / 2 : tm * tn;   // lower: C is square
+    const int total = per * g.batch * g.batch2;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+      const int z = t / per, u = t - z * per;
+      int by, bx;
+      if (lower) {
+        by = static_cast<int>((sqrtf(8.0f * static_cast<float>(u) + 1.0f) - 1.0f) * 0.5f);
+        while ((by + 1) * (by + 2) / 2 <= u) ++by;
+        while (by * (by + 1) / 2 > u) --by;
+        bx = u - by * (by + 1) / 2;
+      } else {
+        by = u / tn;
+        bx = u - by * tn;
+      }
+      gemm_x6_tile<kTransB>(g, bx, by, z);
+      __syncthreads();   // the next tile refills the LDS stages
+    }
+  } else {
+    const int bx = static_cast<int>((blockIdx.x + blockIdx.y + blockIdx.z) % gridDim.x);
+    gemm_x6_tile<kTransB>(g, bx, blockIdx.y, blockIdx.z);
+  }
+}
+
 }  // namespace
+
+// Dynamic LDS of a CU-limited split-bf16 product: 48 KB static + this exceeds half of the
+// CU's 160 KB, and leaves the 66.5 KB of a 64-wide fp32 tile.
+constexpr size_t kOneWgPerCuLds = 33 * 1024;
 
 gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0 || g.batch2 <= 0) return GPTQ_OK;
@@ -535,7 +573,15 @@ gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
     else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false, 1>), grid, dim3(256), 0, stream, g);
     return GPTQ_OK;
   }
-  if (big && vec4) {
+  if (big && vec4 && g.max_cus > 0 && g.transB && (!(g.flags & kLowerOut) || g.M == g.N)) {
+    // At most max_cus workgroups, each with enough (unused) dynamic LDS that no second one
+    // fits its CU: the product occupies max_cus CUs, one workgroup each, and leaves every
+    // other CU free and every occupied CU room for a 64-wide fp32 tile.
+    const int64_t tm = (g.M + 127) / 128, tn = (g.N + 127) / 128;
+    const int64_t total = ((g.flags & kLowerOut) ? tm * (tm + 1) / 2 : tm * tn) * nz;
+    const int wgs = static_cast<int>(std::min<int64_t>(total, g.max_cus));
+    GPTQ_LAUNCH((gemm_x6_kernel<true, 0, true>), dim3(wgs), dim3(256), kOneWgPerCuLds, stream, g);
+  } else if (big && vec4) {
     if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true, 0>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_x6_kernel<false, 0>), grid, dim3(256), 0, stream, g);
   } else if (big) {

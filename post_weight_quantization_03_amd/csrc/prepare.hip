@@ -537,6 +537,16 @@ gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, in
 // 4, 22.0 with 8).
 int far_group(int nb) { return nb <= 32 ? 2 : 4; }
 
+// CUs a far update may occupy (one workgroup each) out of the 256 of the chip, for d_in up
+// to 4096: the others are left to the chain's diagonal-block kernel (135 KB of LDS: it
+// needs a whole CU), and the occupied ones keep room for the chain's 64-wide products.  On
+// every CU (three workgroups each), a far update holds each chain kernel issued during it
+// until it has finished (attn_proj prepare 2.59 -> 2.51 ms when limited).  Wider layers keep
+// the full-chip far updates: one workgroup per CU runs their long updates 1.5x slower, more
+// than the chain gains (mlp_down prepare 19.5 -> 21.4 ms when limited).
+constexpr int kFarCUs = 240;
+int far_cus(int nb) { return nb <= 32 ? kFarCUs : 0; }
+
 gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc) {
   const int nb = sc.nb, batch = sc.batch;
   const int G = far_group(nb);
@@ -591,6 +601,7 @@ gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv,
       u.B = u.A; u.ldb = d_in; u.sB = bsl;
       u.C = block_at(A, d_in, k + 3, k + 3); u.ldc = d_in; u.sC = dd;
       u.alpha = -1.0f; u.beta = 1.0f; u.transB = 1; u.flags = kLowerOut;
+      u.max_cus = far_cus(nb);
       if ((st = gemm_f32(u, s1)) != GPTQ_OK) return st;
       GPTQ_HIP_TRY(hipEventRecord(far_done[nfar & 1], s1));
       last_k[0] = last_k[1];
