@@ -149,6 +149,27 @@ def test_dead_inputs():
     parity.check_problem(spec, Ws[0], X, g, 0)
 
 
+def test_degenerate_weight_rows():
+    # rows the grid fit must survive: all zero (scale floored at 1e-8, every code at the zero
+    # point), constant positive and negative rows (every value on a grid end), values far
+    # below the scale floor, and one huge outlier in an otherwise small row
+    spec = synth.scaled("attn_proj", d_out=24, d_in=256, n_tokens=1200, seq_len=600)
+    announce("degenerate weight rows")
+    Ws, Xs = parity.make_inputs(spec)
+    Wf = R.widen(Ws[0], spec.dtype).astype(np.float32)
+    Wf[0] = 0.0
+    Wf[1] = 0.25
+    Wf[2] = -0.3
+    Wf[3] = 1e-12 * np.sign(Wf[3])
+    Wf[4, 17] = 40.0
+    Wb = synth.f32_to_bf16_bits(Wf)
+    g = parity.run_gpu(spec, [Wb], Xs)
+    parity.check_problem(spec, Wb, Xs[0], g, 0)
+    zeros, codes = g["zeros"][0], g["codes"][0]
+    assert np.all(codes[0] == zeros[:, 0][g["g_idx"][0]])          # the zero row: every code at its zero point
+    assert np.all(g["scales"][0][:, 0] == np.float32(1e-8))
+
+
 def test_not_spd_is_reported():
     announce("not SPD: damp 0, fewer tokens than inputs")
     import torch
