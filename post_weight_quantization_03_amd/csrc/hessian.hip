@@ -46,9 +46,9 @@ constexpr int SYRK_WAVES = 8;
 constexpr int kMinTokensPerSplit = 2048;
 // At most this many tokens per slice: the workgroups of a round stream their panels
 // together, and the longer a slice the further apart they drift, so that panels fetched
-// for one are gone from the caches before the others read them (mlp_down SYRK 46.1 ms with
-// 4 slices of 65536 tokens, 45.6 with 8, 44.3 with 16 of 16384; attn_proj's 15 slices of
-// 8738 tokens already fill its rounds).
+// for one are gone from the caches before the others read them (d_in 14336 over 262144
+// tokens: SYRK 46.1 ms with 4 slices of 65536 tokens, 45.6 with 8, 44.3 with 16 of 16384;
+// d_in 4096 over 131072 tokens: 15 slices of 8738 tokens already fill its rounds).
 constexpr int64_t kMaxTokensPerSplit = 16384;
 
 // Lower tiles (J <= I) of the tile rectangle rows [r0, r1) x columns [c0, c1).

@@ -531,7 +531,7 @@ gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, in
 
 // Panels per far update.  While the chain of small products is the critical path (d_in <=
 // 4096) two: every fork/join between the streams adds a few microseconds to the chain, and
-// near updates of up to three panels are still short (attn_proj prepare 2.73 ms with one,
+// near updates of up to three panels are still short (d_in 4096: prepare 2.73 ms with one,
 // 2.63 with two, 2.66 with three).  Four for wide layers, where the trailing passes bound
 // the factorization (d_in 14336: 26.9 ms with one pass per panel, 22.5 with 2, 21.4 with
 // 4, 22.0 with 8).
@@ -541,9 +541,9 @@ int far_group(int nb) { return nb <= 32 ? 2 : 4; }
 // to 4096: the others are left to the chain's diagonal-block kernel (135 KB of LDS: it
 // needs a whole CU), and the occupied ones keep room for the chain's 64-wide products.  On
 // every CU (three workgroups each), a far update holds each chain kernel issued during it
-// until it has finished (attn_proj prepare 2.59 -> 2.51 ms when limited).  Wider layers keep
+// until it has finished (d_in 4096: prepare 2.59 -> 2.51 ms when limited).  Wider layers keep
 // the full-chip far updates: one workgroup per CU runs their long updates 1.5x slower, more
-// than the chain gains (mlp_down prepare 19.5 -> 21.4 ms when limited).
+// than the chain gains (d_in 14336: prepare 19.5 -> 21.4 ms when limited).
 constexpr int kFarCUs = 240;
 int far_cus(int nb) { return nb <= 32 ? kFarCUs : 0; }
 
