@@ -38,6 +38,22 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
   (f(std::integral_constant<int, I>{}), ...);
 }
 
+// store(i, load(i)) for i = t, t + NT, t + 2 NT, ... < n, the loads of up to B consecutive
+// iterations issued before their stores: a plain loop waits for each global load before
+// its LDS store, one full load latency per iteration.
+template <int NT, int B = 8, typename Load, typename Store>
+__device__ __forceinline__ void batched_copy(int t, int n, Load&& load, Store&& store) {
+  for (int base = t; base < n; base += NT * B) {
+    decltype(load(0)) v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (base + NT * u < n) v[u] = load(base + NT * u);
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (base + NT * u < n) store(base + NT * u, v[u]);
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void gather_reversed_kernel(const float* __res
   const int e = blockIdx.y, t = threadIdx.x;
   const int32_t* pe = perm + static_cast<int64_t>(e) * d_in;
   // indices are clamped so that a malformed permutation can never address outside H
-  for (int c = t; c < d_in; c += 256) sidx[c] = static_cast<uint16_t>(min(max(pe[d_in - 1 - c], 0), d_in - 1));
+  batched_copy<256>(t, d_in, [&](int c) { return pe[d_in - 1 - c]; },
+                    [&](int c, int32_t p) { sidx[c] = static_cast<uint16_t>(min(max(p, 0), d_in - 1)); });
   const float* He = H + static_cast<int64_t>(e) * bsh;
   for (int i = 0; i < GATHER_ROWS; ++i) {
     const int r = blockIdx.x * GATHER_ROWS + i;
@@ -127,10 +128,10 @@ __global__ __launch_bounds__(256) void gather_reversed_kernel(const float* __res
     const int pr = sidx[r];
     const float* src = He + static_cast<int64_t>(pr) * d_in;
     if constexpr (kVec) {
-      for (int c4 = t; c4 < d_in / 4; c4 += 256)
-        reinterpret_cast<float4*>(srow)[c4] = reinterpret_cast<const float4*>(src)[c4];
+      batched_copy<256>(t, d_in / 4, [&](int c4) { return reinterpret_cast<const float4*>(src)[c4]; },
+                        [&](int c4, float4 v) { reinterpret_cast<float4*>(srow)[c4] = v; });
     } else {
-      for (int c = t; c < d_in; c += 256) srow[c] = src[c];
+      batched_copy<256>(t, d_in, [&](int c) { return src[c]; }, [&](int c, float v) { srow[c] = v; });
     }
     __syncthreads();
     const int cend = min(d_in, (r / NB + 1) * NB);

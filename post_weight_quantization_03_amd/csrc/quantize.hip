@@ -51,37 +51,40 @@ __global__ __launch_bounds__(256) void permute_weight_staged_kernel(const T* __r
   __shared__ __attribute__((aligned(16))) float srow[DMAX];
   __shared__ uint16_t sidx[DMAX];
   const int e = blockIdx.y, t = threadIdx.x;
-  for (int j = t; j < d_in; j += 256) {
-    // a malformed permutation is clamped into range rather than addressing outside W
-    const int c = min(max(perm[static_cast<int64_t>(e) * d_in + j], 0), d_in - 1);
-    sidx[j] = dead[static_cast<int64_t>(e) * d_in + c] ? kDeadCol : static_cast<uint16_t>(c);
-  }
+  // a malformed permutation is clamped into range rather than addressing outside W
+  batched_copy<256>(
+      t, d_in,
+      [&](int j) -> uint16_t {
+        const int c = min(max(perm[static_cast<int64_t>(e) * d_in + j], 0), d_in - 1);
+        return dead[static_cast<int64_t>(e) * d_in + c] ? kDeadCol : static_cast<uint16_t>(c);
+      },
+      [&](int j, uint16_t v) { sidx[j] = v; });
   for (int i = 0; i < STAGE_ROWS; ++i) {
     const int r = blockIdx.x * STAGE_ROWS + i;
     if (r >= d_out) break;
     __syncthreads();  // sidx written / the previous row fully consumed
     const T* src = W + static_cast<int64_t>(e) * bsw + static_cast<int64_t>(r) * ldw;
     if constexpr (kVec && sizeof(T) == 2) {
-      for (int c8 = t; c8 < d_in / 8; c8 += 256) {
-        const uint4 v = reinterpret_cast<const uint4*>(src)[c8];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
+      batched_copy<256>(t, d_in / 8, [&](int c8) { return reinterpret_cast<const uint4*>(src)[c8]; },
+                        [&](int c8, uint4 v) {
+                          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+                          float f[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          T lo, hi;
-          lo.bits = static_cast<uint16_t>(u[q] & 0xFFFFu);
-          hi.bits = static_cast<uint16_t>(u[q] >> 16);
-          f[2 * q] = load_as_f32(&lo);
-          f[2 * q + 1] = load_as_f32(&hi);
-        }
-        reinterpret_cast<float4*>(srow)[2 * c8] = make_float4(f[0], f[1], f[2], f[3]);
-        reinterpret_cast<float4*>(srow)[2 * c8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
-      }
+                          for (int q = 0; q < 4; ++q) {
+                            T lo, hi;
+                            lo.bits = static_cast<uint16_t>(u[q] & 0xFFFFu);
+                            hi.bits = static_cast<uint16_t>(u[q] >> 16);
+                            f[2 * q] = load_as_f32(&lo);
+                            f[2 * q + 1] = load_as_f32(&hi);
+                          }
+                          reinterpret_cast<float4*>(srow)[2 * c8] = make_float4(f[0], f[1], f[2], f[3]);
+                          reinterpret_cast<float4*>(srow)[2 * c8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
+                        });
     } else if constexpr (kVec) {
-      for (int c4 = t; c4 < d_in / 4; c4 += 256)
-        reinterpret_cast<float4*>(srow)[c4] = reinterpret_cast<const float4*>(src)[c4];
+      batched_copy<256>(t, d_in / 4, [&](int c4) { return reinterpret_cast<const float4*>(src)[c4]; },
+                        [&](int c4, float4 v) { reinterpret_cast<float4*>(srow)[c4] = v; });
     } else {
-      for (int c = t; c < d_in; c += 256) srow[c] = load_as_f32(src + c);
+      batched_copy<256>(t, d_in, [&](int c) { return load_as_f32(src + c); }, [&](int c, float v) { srow[c] = v; });
     }
     __syncthreads();
     float* dst = Wp + (static_cast<int64_t>(e) * d_out + r) * d_in;
@@ -448,19 +451,20 @@ __global__ __launch_bounds__(256) void unpermute_staged_kernel(const uint8_t* __
   __shared__ __attribute__((aligned(16))) uint8_t srow[DMAX];
   __shared__ uint16_t sidx[DMAX];
   const int e = blockIdx.y, t = threadIdx.x;
-  for (int c = t; c < d_in; c += 256) {
-    const int j = min(max(inv[static_cast<int64_t>(e) * d_in + c], 0), d_in - 1);
-    sidx[c] = static_cast<uint16_t>(j);
-    if (blockIdx.x == 0) g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? (by_orig ? c : j) / group : 0;
-  }
+  batched_copy<256>(t, d_in, [&](int c) { return min(max(inv[static_cast<int64_t>(e) * d_in + c], 0), d_in - 1); },
+                    [&](int c, int j) {
+                      sidx[c] = static_cast<uint16_t>(j);
+                      if (blockIdx.x == 0)
+                        g_idx[static_cast<int64_t>(e) * d_in + c] = group > 0 ? (by_orig ? c : j) / group : 0;
+                    });
   for (int i = 0; i < STAGE_ROWS; ++i) {
     const int r = blockIdx.x * STAGE_ROWS + i;
     if (r >= d_out) break;
     __syncthreads();
     const int64_t ro = (static_cast<int64_t>(e) * d_out + r) * d_in;
     // codes_p rows start at multiples of d_in (a multiple of 128) in a 256-byte aligned workspace
-    for (int c16 = t; c16 < d_in / 16; c16 += 256)
-      reinterpret_cast<uint4*>(srow)[c16] = reinterpret_cast<const uint4*>(codes_p + ro)[c16];
+    batched_copy<256>(t, d_in / 16, [&](int c16) { return reinterpret_cast<const uint4*>(codes_p + ro)[c16]; },
+                      [&](int c16, uint4 v) { reinterpret_cast<uint4*>(srow)[c16] = v; });
     __syncthreads();
     if constexpr (kVec) {
       for (int c = 16 * t; c < d_in; c += 4096) {
