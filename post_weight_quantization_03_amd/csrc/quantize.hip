@@ -525,23 +525,39 @@ struct SweepShape {
 
 // The U block takes 64 KB of LDS, so at most two workgroups share a CU.  With rows enough
 // for about one wave per SIMD at 4 lanes per row (16 rows per wave), rows get 4 lanes;
-// else 16.  Then the largest workgroup that still gives every CU at least one (at most
-// 512 threads for groups of 64 at 4 lanes per row, whose registers would not fit 1024).  The small
-// groups (16, 32) keep 16 lanes and 256 threads: their sweeps need too many registers
-// for more than one wave per SIMD.
+// else 16.  At 16 lanes, the largest workgroup that still gives every CU at least one.  At
+// 4 lanes the sweep is bound by VALU issue and LDS reads, so its time goes with the rows
+// the busiest CU takes, ceil(workgroups / 256) x rows per workgroup: of the workgroup sizes
+// below, the one that makes this smallest (64 experts of 1408 rows: 704 threads, 8 x 64
+// workgroups of 176 rows in two even rounds, where 1024 threads left a third of the chip
+// idle in the second round).  Groups of 64 at 4 lanes per row stop at 512 threads (their
+// registers would not fit more).  The small groups (16, 32) keep 16 lanes and 256
+// threads: their sweeps need too many registers for more than one wave per SIMD.
+constexpr int kCUs = 256;
 SweepShape sweep_shape(int G, bool stat, int batch, int d_out) {
   // static groups keep 16 lanes per row: each lane also holds the grids of its columns
   const bool wide_ok = !stat && (G == 0 || G == 64 || G == 128);
   const int64_t rows = static_cast<int64_t>(batch) * d_out;
   const int lpr = (wide_ok && rows / 16 >= 768) ? 4 : 16;
   int nt = 256;
-  if (wide_ok) {
+  if (wide_ok && lpr == 16) {
     for (int cand : {1024, 512}) {
-      if (cand == 1024 && lpr == 4 && G == 64) continue;   // would spill registers
       const int rpw = cand / lpr;
-      if (static_cast<int64_t>((d_out + rpw - 1) / rpw) * batch >= 256) {
+      if (static_cast<int64_t>((d_out + rpw - 1) / rpw) * batch >= kCUs) {
         nt = cand;
         break;
+      }
+    }
+  } else if (wide_ok) {
+    int64_t best = -1;
+    for (int cand : {1024, 704, 512, 256}) {
+      if (G == 64 && cand > 512) continue;   // would spill registers
+      const int rpw = cand / lpr;
+      const int64_t wgs = static_cast<int64_t>((d_out + rpw - 1) / rpw) * batch;
+      const int64_t cost = (wgs + kCUs - 1) / kCUs * rpw;
+      if (best < 0 || cost < best) {
+        best = cost;
+        nt = cand;
       }
     }
   }
@@ -585,6 +601,7 @@ gptq_status launch_sweep_nt(const SweepShape& sh, hipStream_t stream, const Swee
     GPTQ_SWEEP(512, 16)   // 1024 threads at 16 lanes: never chosen (4 lanes take over first)
     if constexpr (G != 64) {
       GPTQ_SWEEP(1024, 4)
+      GPTQ_SWEEP(704, 4)
     }
     GPTQ_SWEEP(512, 4)
     GPTQ_SWEEP(256, 4)
