@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) void keys_kernel(const double* __restrict__ di
 
 // rank(c) = #{j: key_j > key_c} + #{j < c: key_j == key_c}, the position of c in a stable
 // descending sort.  Block (x, y): 256 candidates c against a slice of RANK_SLICE keys j;
-// the integer partial counts are summed with atomics (order-independent, exact).
-constexpr int RANK_SLICE = 512;
+// the integer partial counts are summed with atomics (order-independent, exact).  Slices of
+// 256 keys give d_in 4096 its 256 workgroups, one per CU.
+constexpr int RANK_SLICE = 256;
 __global__ __launch_bounds__(256) void actorder_rank_kernel(const double* __restrict__ key, int d_in,
                                                             int32_t* __restrict__ rank) {
   __shared__ double sk[RANK_SLICE];
