@@ -512,6 +512,37 @@ __device__ __forceinline__ void gemm_x6_tile(const GemmArgs& g, int bx, int by, 
     }
 }
 
+// Tile of this workgroup.  Workgroups start in linear order (x fastest), dealt to the 8
+// XCDs round-robin (XCD = id % 8), so XCD x runs ids x, x + 8, x + 16, ...  The tiles are
+// ordered in bands of kBand tile rows (the rows of all batch entries stacked), column by
+// column inside a band, and XCD x takes the x-th of 8 consecutive runs of that order, one
+// tile per id in its turn.  The ~96 workgroups an XCD holds at once then cover about 24
+// columns of 4 rows, whose 28 operand panels its L2 shares, instead of tiles strewn over
+// the grid.  col_bands: the same with rows and columns exchanged (bands of kBand tile
+// columns, row by row), for products whose work per tile grows with the row, so that
+// every band, and so every XCD's run, holds light and heavy rows alike.
+constexpr int kBand = 4;
+__device__ __forceinline__ void xcd_band_tile(bool col_bands, int& bx, int& by, int& bz) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int total = nx * ny * static_cast<int>(gridDim.z);
+  const int lin = static_cast<int>(blockIdx.x) + nx * (static_cast<int>(blockIdx.y) + ny * static_cast<int>(blockIdx.z));
+  const int x = lin & 7, s = lin >> 3;
+  // ids on XCD x: ceil((total - x) / 8); the runs before x hold those of XCDs 0 .. x-1
+  const int q = total >> 3, r = total & 7;
+  const int t = x * q + min(x, r) + s;
+  const int rows = ny * static_cast<int>(gridDim.z);
+  const int lines = col_bands ? nx : rows;     // what the bands cut
+  const int across = col_bands ? rows : nx;    // what a band runs along
+  const int band = t / (kBand * across);
+  const int hb = min(kBand, lines - band * kBand);
+  const int u = t - band * kBand * across;
+  const int along = u / hb, line = band * kBand + u % hb;
+  const int row = col_bands ? along : line;
+  bx = col_bands ? line : along;
+  by = row % ny;
+  bz = row / ny;
+}
+
 // kPersist: a grid of fewer workgroups than tiles, each taking every gridDim.x-th tile in
 // turn (lower tiles only with kLowerOut, row by row); otherwise one tile per workgroup
 // (column index rotated by the row and batch index: workgroups are dealt to the 8 XCDs
@@ -539,6 +570,11 @@ __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
       gemm_x6_tile<kTransB>(g, bx, by, z);
       __syncthreads();   // the next tile refills the LDS stages
     }
+  } else if (kRole == 1 || g.flags == 0 || g.flags == kBLower || g.flags == kALower) {
+    // rectangular products, and triangular ones whose work varies along one axis only
+    int bx, by, bz;
+    xcd_band_tile(g.flags == kALower, bx, by, bz);
+    gemm_x6_tile<kTransB>(g, bx, by, bz);
   } else {
     const int bx = static_cast<int>((blockIdx.x + blockIdx.y + blockIdx.z) % gridDim.x);
     gemm_x6_tile<kTransB>(g, bx, blockIdx.y, blockIdx.z);
