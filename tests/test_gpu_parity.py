@@ -53,6 +53,8 @@ CASES = {
     "group128_4_lanes_704": synth.scaled("moe", d_out=1408, d_in=256, n_tokens=300, batch=32, seq_len=300),
     "per_row_4_lanes_704": synth.scaled("moe", d_out=1408, d_in=256, n_tokens=300, batch=32, seq_len=300,
                                         group_size=-1),
+    # 1024 threads at 4 lanes per row (4 x 64 = 256 workgroups of 256 rows)
+    "group128_4_lanes_1024": synth.scaled("moe", d_out=1024, d_in=128, n_tokens=300, batch=64, seq_len=300),
     # fp16 inputs (the f16 matrix-core SYRK, fp16 channel energies and weight permutes)
     "fp16_attn_scaled": synth.scaled("attn_proj", d_out=136, d_in=384, n_tokens=3000, seq_len=1000, dtype="f16"),
     "fp16_moe_scaled": synth.scaled("moe", d_out=64, d_in=256, n_tokens=900, batch=3, seq_len=300, dtype="f16",
