@@ -544,10 +544,11 @@ __device__ __forceinline__ void xcd_band_tile(bool col_bands, int& bx, int& by, 
 }
 
 // kPersist: a grid of fewer workgroups than tiles, each taking every gridDim.x-th tile in
-// turn (lower tiles only with kLowerOut, row by row); otherwise one tile per workgroup
-// (column index rotated by the row and batch index: workgroups are dealt to the 8 XCDs
-// round-robin by linear id, and with triangular operands or a lower-only output the work
-// of a tile depends on its column).
+// turn (lower tiles only with kLowerOut, row by row).  Otherwise one tile per workgroup:
+// the lazy updates, plain products and those with one triangular operand in the XCD band
+// order above; lower-only outputs (and the remaining flag combinations) with the column
+// index rotated by the row and batch index, so that the XCDs, dealt workgroups round-robin
+// by linear id, mix tiles whose work depends on the column.
 template <bool kTransB, int kRole, bool kPersist = false>
 __global__ __launch_bounds__(256, 2) void gemm_x6_kernel(GemmArgs g) {
   if constexpr (kPersist) {
