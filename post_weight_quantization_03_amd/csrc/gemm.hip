@@ -169,6 +169,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
+  const int l32 = lane & 31, kh = lane >> 5;
+  // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // 64-wide tiles (one 32 x 32 block per wave, short K loops): with beta != 0 the old C
+  // values are loaded before the K loop, so that their latency overlaps it rather than
+  // following it (C never overlaps A or B).
+  const bool has_beta = g.beta != 0.0f;
+  constexpr bool kPreC = (MB == 1);
+  float preC[16];
+  if constexpr (kPreC) {
+    const int n = n0 + (GT / 2) * wn + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + (GT / 2) * wm + 8 * (r >> 2) + 4 * kh + (r & 3);
+      preC[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
+    }
+  }
   const int nk = ke > kb ? (ke - kb + GK - 1) / GK : 0;
   if (nk > 0) {
     load_rows(A, g.lda, m0, g.M, kb, ra);
@@ -177,7 +193,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     store_b(sB[0], kb);
   }
   __syncthreads();
-  const int l32 = lane & 31, kh = lane >> 5;
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < nk;
@@ -206,11 +221,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  // With beta != 0 the 16 old values of a block are all loaded before any of its stores:
-  // element by element, every load would have to wait for the previous store (the
-  // compiler cannot tell that they never overlap).
-  const bool has_beta = g.beta != 0.0f;
+  // With beta != 0 (128-wide tiles) the 16 old values of a block are all loaded before any
+  // of its stores: element by element, every load would have to wait for the previous
+  // store (the compiler cannot tell that they never overlap).
 #pragma unroll
   for (int bm = 0; bm < MB; ++bm)
 #pragma unroll
@@ -220,7 +233,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + (GT / 2) * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
-        old[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
+        if constexpr (kPreC) old[r] = preC[r];
+        else old[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
