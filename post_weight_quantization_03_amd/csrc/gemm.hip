@@ -503,27 +503,36 @@ __device__ __forceinline__ void gemm_x6_tile(const GemmArgs& g, int bx, int by, 
   }
 
   // 32x32 accumulator layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // With beta != 0 each block's 16 old values are loaded before the previous block's
+  // stores, so that the loads of the next block are in flight while a block is written
+  // (the compiler cannot move them there itself, not knowing that the blocks never
+  // overlap); all four blocks at once would keep 64 more addresses and values live.
   const bool has_beta = g.beta != 0.0f;
+  float old[2][16];
+  auto load_old = [&](int blk, float* o) {
+    const int bm = blk >> 1, bn = blk & 1;
+    const int n = n0 + 64 * wn + 32 * bn + l32;
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
+      o[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
+    }
+  };
+  load_old(0, old[0]);
+  static_for(std::make_integer_sequence<int, 4>{}, [&](auto bc) {
+    constexpr int blk = decltype(bc)::value;
+    constexpr int bm = blk >> 1, bn = blk & 1;
+    if constexpr (blk + 1 < 4) load_old(blk + 1, old[(blk + 1) & 1]);
+    const int n = n0 + 64 * wn + 32 * bn + l32;
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      const int n = n0 + 64 * wn + 32 * bn + l32;
-      float old[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
-        old[r] = (has_beta && m < g.M && n < g.N) ? C[static_cast<int64_t>(m) * g.ldc + n] : 0.0f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (m < g.M && n < g.N) {
-          const float v = g.alpha * acc[bm][bn][r];
-          C[static_cast<int64_t>(m) * g.ldc + n] = has_beta ? fmaf(g.beta, old[r], v) : v;
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 64 * wm + 32 * bm + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (m < g.M && n < g.N) {
+        const float v = g.alpha * acc[bm][bn][r];
+        C[static_cast<int64_t>(m) * g.ldc + n] = has_beta ? fmaf(g.beta, old[blk & 1][r], v) : v;
       }
     }
+  });
 }
 
 // Tile of this workgroup.  Workgroups start in linear order (x fastest), dealt to the 8
