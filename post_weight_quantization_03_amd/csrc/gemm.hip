@@ -71,7 +71,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  float4 ra[RQ], rb[RQ];
+  // loads run two stages ahead through a ring of two register sets
+  float4 ra[2][RQ], rb[2][RQ];
   // Row-major tile [GT rows][GK k] read as float4: half a wave covers 4 rows x 8 k-vectors
   // (row lr + RS q, k 4 lc .. 4 lc + 3), which makes its transposing LDS stores conflict-free.
   constexpr int RS = 1024 / GK;  // rows per pass of the workgroup
@@ -152,13 +153,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       *reinterpret_cast<float4*>(&s[k][4 * (tid % NV)]) = v;
     }
   };
-  auto load_b = [&](int k0) {
-    if constexpr (kTransB) load_rows(B, g.ldb, n0, g.N, k0, rb);
-    else load_kmajor(k0, rb);
+  auto load_b = [&](int k0, float4* r) {
+    if constexpr (kTransB) load_rows(B, g.ldb, n0, g.N, k0, r);
+    else load_kmajor(k0, r);
   };
-  auto store_b = [&](float (*s)[GPB], int k0) {
-    if constexpr (kTransB) store_rows(s, rb, n0, g.N, k0);
-    else store_kmajor(s, rb, k0);
+  auto store_b = [&](float (*s)[GPB], const float4* r, int k0) {
+    if constexpr (kTransB) store_rows(s, r, n0, g.N, k0);
+    else store_kmajor(s, r, k0);
   };
 
   f32x16 acc[MB][MB];
@@ -187,18 +188,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
   const int nk = ke > kb ? (ke - kb + GK - 1) / GK : 0;
   if (nk > 0) {
-    load_rows(A, g.lda, m0, g.M, kb, ra);
-    load_b(kb);
-    store_rows(sA[0], ra, m0, g.M, kb);
-    store_b(sB[0], kb);
+    load_rows(A, g.lda, m0, g.M, kb, ra[0]);
+    load_b(kb, rb[0]);
+    if (nk > 1) {
+      load_rows(A, g.lda, m0, g.M, kb + GK, ra[1]);
+      load_b(kb + GK, rb[1]);
+    }
+    store_rows(sA[0], ra[0], m0, g.M, kb);
+    store_b(sB[0], rb[0], kb);
   }
   __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nk;
-    if (more) {
-      load_rows(A, g.lda, m0, g.M, kb + (s + 1) * GK, ra);
-      load_b(kb + (s + 1) * GK);
+  // iteration s: loads of stage s + 2 into the register set of stage s (stored to LDS one
+  // iteration earlier) | products of LDS buffer s % 2 | stage s + 1 from the other register
+  // set into the other buffer.  Unrolled by two so that the register sets are fixed.
+  auto iteration = [&](int s, auto bc) {
+    constexpr int buf = decltype(bc)::value;
+    if (s + 2 < nk) {
+      load_rows(A, g.lda, m0, g.M, kb + (s + 2) * GK, ra[buf]);
+      load_b(kb + (s + 2) * GK, rb[buf]);
     }
 #pragma unroll
     for (int kk = 0; kk < GK / 2; ++kk) {
@@ -214,11 +221,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
         for (int bn = 0; bn < MB; ++bn)
           acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[bm], bv[bn], acc[bm][bn], 0, 0, 0);
     }
-    if (more) {
-      store_rows(sA[buf ^ 1], ra, m0, g.M, kb + (s + 1) * GK);
-      store_b(sB[buf ^ 1], kb + (s + 1) * GK);
+    if (s + 1 < nk) {
+      store_rows(sA[buf ^ 1], ra[buf ^ 1], m0, g.M, kb + (s + 1) * GK);
+      store_b(sB[buf ^ 1], rb[buf ^ 1], kb + (s + 1) * GK);
     }
     __syncthreads();
+  };
+  for (int s = 0; s < nk; s += 2) {
+    iteration(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nk) iteration(s + 1, std::integral_constant<int, 1>{});
   }
 
   // With beta != 0 (128-wide tiles) the 16 old values of a block are all loaded before any
