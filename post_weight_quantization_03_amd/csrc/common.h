@@ -138,13 +138,15 @@ gptq_status pack_enqueue(int batch, int d_out, int d_in, int n_groups, const uin
 constexpr int kTimedKinds = 5;
 void timing_pair(gptq_timed_kernel kind, hipEvent_t* start, hipEvent_t* stop);
 
-// A second stream per device for work that can overlap the caller's stream; two events
-// fork work onto it and join it back.  Created on first use, kept for the life of the
-// process.  Callers hold side_mutex() while they enqueue on it.
+// Two more streams per device for work that can overlap the caller's stream, with events
+// that fork work onto them and join it back.  Created on first use, kept for the life of
+// the process.  Callers hold side_mutex() while they enqueue on them.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   hipEvent_t join2 = nullptr;   // a second join event, for two side-stream stages in flight
+  hipStream_t s2 = nullptr;     // the second side stream
+  hipEvent_t fork2 = nullptr, join3 = nullptr;
 };
 std::mutex& side_mutex();
 gptq_status side_stream(SideStream** out);   // of the current device

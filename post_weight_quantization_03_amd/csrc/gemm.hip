@@ -644,14 +644,15 @@ gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
     else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false, 1>), grid, dim3(256), 0, stream, g);
     return GPTQ_OK;
   }
-  if (big && vec4 && g.max_cus > 0 && g.transB && (!(g.flags & kLowerOut) || g.M == g.N)) {
+  if (big && vec4 && g.max_cus > 0 && (!(g.flags & kLowerOut) || g.M == g.N)) {
     // At most max_cus workgroups, each with enough (unused) dynamic LDS that no second one
     // fits its CU: the product occupies max_cus CUs, one workgroup each, and leaves every
     // other CU free and every occupied CU room for a 64-wide fp32 tile.
     const int64_t tm = (g.M + 127) / 128, tn = (g.N + 127) / 128;
     const int64_t total = ((g.flags & kLowerOut) ? tm * (tm + 1) / 2 : tm * tn) * nz;
     const int wgs = static_cast<int>(std::min<int64_t>(total, g.max_cus));
-    GPTQ_LAUNCH((gemm_x6_kernel<true, 0, true>), dim3(wgs), dim3(256), kOneWgPerCuLds, stream, g);
+    if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true, 0, true>), dim3(wgs), dim3(256), kOneWgPerCuLds, stream, g);
+    else GPTQ_LAUNCH((gemm_x6_kernel<false, 0, true>), dim3(wgs), dim3(256), kOneWgPerCuLds, stream, g);
   } else if (big && vec4) {
     if (g.transB) GPTQ_LAUNCH((gemm_x6_kernel<true, 0>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_x6_kernel<false, 0>), grid, dim3(256), 0, stream, g);

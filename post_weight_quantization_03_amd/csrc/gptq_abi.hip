@@ -60,12 +60,11 @@ gptq_status side_stream(SideStream** out) {
   GPTQ_HIP_TRY(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDevices) return GPTQ_ERR_HIP;
   SideStream& ss = g_side[dev];
-  if (ss.s == nullptr) {
-    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
-    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
-    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
-    GPTQ_HIP_TRY(hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming));
-  }
+  // each handle created once; a failed creation is retried on the next call
+  for (hipStream_t* st : {&ss.s, &ss.s2})
+    if (*st == nullptr) GPTQ_HIP_TRY(hipStreamCreateWithFlags(st, hipStreamNonBlocking));
+  for (hipEvent_t* ev : {&ss.fork, &ss.join, &ss.join2, &ss.fork2, &ss.join3})
+    if (*ev == nullptr) GPTQ_HIP_TRY(hipEventCreateWithFlags(ev, hipEventDisableTiming));
   *out = &ss;
   return GPTQ_OK;
 }

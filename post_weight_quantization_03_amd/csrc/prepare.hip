@@ -12,8 +12,9 @@
 //      positive-diagonal upper factor the pages obtain with chol / cholesky_inverse / chol,
 //      at 2/3 d^3 instead of 4/3 d^3 flops.
 //
-// Cholesky blocked by 128 columns (chol_blocked below), then the triangular inverse by
-// doubling (trtri_doubling): one workgroup factors and inverts each 128-column diagonal
+// Cholesky blocked by 128 columns (chol_blocked below) and the triangular inverse by
+// doubling (TriInverse, its early parts beside the factorization's later steps): one
+// workgroup factors and inverts each 128-column diagonal
 // block in LDS (by recursive halving inside the kernel); everything else is fp32
 // matrix-core products.  A non-positive or non-finite pivot sets a device flag that
 // the host reads back (GPTQ_ERR_NOT_SPD).
@@ -430,12 +431,22 @@ __global__ __launch_bounds__(256) void reverse_to_upper_kernel(const float* __re
   }
 }
 
-// Floats of T per problem for trtri_doubling: the largest level, (full groups + 1) h^2.
+// Groups of the triangular inverse's doubling level with halves of hb blocks (nb blocks in
+// all): the full groups of 2 hb blocks, then a ragged last one when the blocks left over
+// exceed one half.
+int tri_groups(int nb, int hb) {
+  const int full = nb / (2 * hb);
+  return full + (nb - full * 2 * hb > hb ? 1 : 0);
+}
+
+// Floats of T per problem for the triangular inverse: an h x h product per group and level,
+// kept from the T product of a group to its X21 product (the two may be issued at different
+// points of the factorization).
 size_t trtri_t_floats(int nb) {
   size_t m = 0;
   for (int hb = 1; hb < nb; hb *= 2) {
     const size_t h = static_cast<size_t>(hb) * NB;
-    m = std::max(m, static_cast<size_t>(nb / (2 * hb) + 1) * h * h);
+    m += static_cast<size_t>(tri_groups(nb, hb)) * h * h;
   }
   return m;
 }
@@ -465,6 +476,81 @@ PrepWs carve(void* ws, int batch, int d_in) {
   w.bytes = cv.used;
   return w;
 }
+
+// X = L^-1 from L and its inverted diagonal blocks, by doubling: at the level of groups of
+// 2 hb blocks (hb = 1, 2, 4, ...), group [o, o + 2h) (h = 128 hb) gets
+//   T = L21 X11,   X21 = -X22 T
+// (X11 = L11^-1 lower: the K range of an output column of T starts at it; X22 lower: the
+// K range of an output row of X21 ends at it); a ragged last group has a full first half
+// and a shorter second half, itself inverted at the levels below.  T needs the columns of L
+// under the group's first half and that half's inverse only, so it can run as soon as the
+// factorization has passed the first half; X21 waits for the second half.  issue(ready)
+// enqueues every product of the inverse whose operands lie in the first `ready` factored
+// block columns and that is not yet enqueued, level by level upward, one batched product
+// per run of groups: called as the factorization proceeds, the early levels and the T
+// products overlap the rest of the factorization; called once with ready = nb, it is the
+// plain level-by-level order.  Each group's T has its own place (trtri_t_floats).
+struct TriInverse {
+  static constexpr int kLevels = 32;
+  int d_in, nb, batch;
+  const float* L;
+  int64_t bsl;
+  float* Linv;
+  float* T;
+  int next_t[kLevels] = {}, next_x[kLevels] = {};   // per level: first group not enqueued
+
+  gptq_status issue(int ready, hipStream_t stream, int max_cus, int max_hb = 1 << 30) {
+    const int64_t dd = static_cast<int64_t>(d_in) * d_in;
+    const int64_t tstride = static_cast<int64_t>(trtri_t_floats(nb));   // T floats per problem
+    int64_t tbase = 0;
+    int lv = 0;
+    for (int hb = 1; hb < nb && hb <= max_hb; hb *= 2, ++lv) {
+      const int h = hb * NB;
+      const int full = nb / (2 * hb);
+      const int groups = tri_groups(nb, hb);
+      const int64_t gs = static_cast<int64_t>(2 * h) * (d_in + 1);   // next group, same level
+      const int64_t hh = static_cast<int64_t>(h) * h;
+      float* Tl = T + tbase;
+      tbase += groups * hh;
+      int t_end = next_t[lv], x_end = next_x[lv];
+      while (t_end < groups && t_end * 2 * hb + hb <= ready) ++t_end;
+      while (x_end < groups && (x_end < full ? (x_end + 1) * 2 * hb <= ready : ready == nb)) ++x_end;
+      // groups [a, b) in runs of full groups, the ragged one alone (a shorter second half)
+      for (int pass = 0; pass < 2; ++pass) {
+        const bool is_t = pass == 0;
+        int a = is_t ? next_t[lv] : next_x[lv];
+        const int b = is_t ? t_end : x_end;
+        while (a < b) {
+          const int e = a < full ? std::min(b, full) : b;
+          const int h2 = a < full ? h : (nb - full * 2 * hb - hb) * NB;
+          const int64_t o = static_cast<int64_t>(a) * 2 * h;
+          GemmArgs g{};
+          g.batch = batch; g.batch2 = e - a; g.max_cus = max_cus;
+          g.M = h2; g.N = h; g.transB = 0;
+          if (is_t) {
+            g.K = h;
+            g.A = L + (o + h) * d_in + o; g.lda = d_in; g.sA = bsl; g.sA2 = gs;
+            g.B = Linv + o * d_in + o; g.ldb = d_in; g.sB = dd; g.sB2 = gs;
+            g.C = Tl + a * hh; g.ldc = h; g.sC = tstride; g.sC2 = hh;
+            g.alpha = 1.0f; g.beta = 0.0f; g.flags = kBLower;
+          } else {
+            g.K = h2;
+            g.A = Linv + (o + h) * d_in + o + h; g.lda = d_in; g.sA = dd; g.sA2 = gs;
+            g.B = Tl + a * hh; g.ldb = h; g.sB = tstride; g.sB2 = hh;
+            g.C = Linv + (o + h) * d_in + o; g.ldc = d_in; g.sC = dd; g.sC2 = gs;
+            g.alpha = -1.0f; g.beta = 0.0f; g.flags = kALower;
+          }
+          gptq_status st = gemm_f32(g, stream);
+          if (st != GPTQ_OK) return st;
+          a = e;
+        }
+      }
+      next_t[lv] = t_end;
+      next_x[lv] = x_end;
+    }
+    return GPTQ_OK;
+  }
+};
 
 // Cholesky of A (lower, in place) into L, blocked by 128 columns, right-looking with
 // lookahead.  For each block column k, on the main stream:
@@ -549,11 +635,19 @@ int far_group(int nb) { return nb <= 32 ? 2 : 4; }
 constexpr int kFarCUs = 240;
 int far_cus(int nb) { return nb <= 32 ? kFarCUs : 0; }
 
-gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc) {
+// Block columns between the points where the triangular inverse's ready products are
+// enqueued beside the factorization, and the CUs they may take there (0: all).
+constexpr int kTriStep = 8;
+constexpr int kTriMaxHb = 1 << 30;
+int tri_cus(int nb) { return 0; }
+
+gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc,
+                         TriInverse& tri) {
   const int nb = sc.nb, batch = sc.batch;
   const int G = far_group(nb);
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
-  hipStream_t s0 = sc.main, s1 = sc.side->s;
+  hipStream_t s0 = sc.main, s1 = sc.side->s, s2 = sc.side->s2;
+  bool tri_forked = false;
   hipEvent_t far_done[2] = {sc.side->join, sc.side->join2};   // far update i records far_done[i % 2]
   // checkpoints of the last two far updates (their checkpoints differ by G >= 1, so when
   // the last one is too recent to cover a column, the one before it does)
@@ -573,6 +667,13 @@ gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv,
     g.C = block_at(L, d_in, k + 1, k); g.ldc = d_in; g.sC = bsl;
     g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower;
     if ((st = gemm_f32(g, s0)) != GPTQ_OK) return st;
+    // columns 0..k of L are final: the inverse's products over them, on the second side stream
+    if ((k + 1) % kTriStep == 0) {
+      GPTQ_HIP_TRY(hipEventRecord(sc.side->fork2, s0));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(s2, sc.side->fork2, 0));
+      if ((st = tri.issue(k + 1, s2, tri_cus(nb), kTriMaxHb)) != GPTQ_OK) return st;
+      tri_forked = true;
+    }
     // near(k) writes column c = k + 1: the last far update covering it has checkpoint <= k - 2
     int F = 0, wait = -1;
     if (nfar >= 1 && last_k[1] <= k - 2) {
@@ -614,52 +715,12 @@ gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv,
   }
   // every far update has been joined by a later near update; join the last one anyway
   if (nfar > 0) GPTQ_HIP_TRY(hipStreamWaitEvent(s0, far_done[(nfar - 1) & 1], 0));
-  return GPTQ_OK;
-}
-
-// X = L^-1 from L and its inverted diagonal blocks, by doubling: at the level of groups of
-// 2 hb blocks (hb = 1, 2, 4, ...), every group [o, o + 2h) whose halves are inverted gets
-//   T = L21 X11,   X21 = -X22 T
-// (X11 = L11^-1 lower: the K range of an output column of T starts at it; X22 lower: the
-// K range of an output row of X21 ends at it).  All full groups of a level go in one
-// batched product each; a ragged last group (a full first half and a shorter second half,
-// itself inverted at the level below) gets its own pair.
-gptq_status trtri_doubling(int d_in, const float* L, int64_t bsl, float* Linv, float* T, int nb, int batch,
-                           hipStream_t stream) {
-  const int64_t dd = static_cast<int64_t>(d_in) * d_in;
-  for (int hb = 1; hb < nb; hb *= 2) {
-    const int h = hb * NB;
-    const int full = nb / (2 * hb);
-    const int tail = nb - full * 2 * hb;                       // blocks of the last group
-    const int64_t tstride = static_cast<int64_t>(full + 1) * h * h;   // T floats per problem
-    auto pair = [&](int o_blk, int h2, int groups, float* Tg) -> gptq_status {
-      const int64_t gs = static_cast<int64_t>(2 * h) * (d_in + 1);   // next group, same level
-      const int o = o_blk * NB;
-      gptq_status st;
-      GemmArgs t{};
-      t.batch = batch; t.batch2 = groups;
-      t.M = h2; t.N = h; t.K = h;
-      t.A = L + static_cast<int64_t>(o + h) * d_in + o; t.lda = d_in; t.sA = bsl; t.sA2 = gs;
-      t.B = Linv + static_cast<int64_t>(o) * d_in + o; t.ldb = d_in; t.sB = dd; t.sB2 = gs;
-      t.C = Tg; t.ldc = h; t.sC = tstride; t.sC2 = static_cast<int64_t>(h) * h;
-      t.alpha = 1.0f; t.beta = 0.0f; t.transB = 0; t.flags = kBLower;
-      if ((st = gemm_f32(t, stream)) != GPTQ_OK) return st;
-      GemmArgs x{};
-      x.batch = batch; x.batch2 = groups;
-      x.M = h2; x.N = h; x.K = h2;
-      x.A = Linv + static_cast<int64_t>(o + h) * d_in + o + h; x.lda = d_in; x.sA = dd; x.sA2 = gs;
-      x.B = Tg; x.ldb = h; x.sB = tstride; x.sB2 = static_cast<int64_t>(h) * h;
-      x.C = Linv + static_cast<int64_t>(o + h) * d_in + o; x.ldc = d_in; x.sC = dd; x.sC2 = gs;
-      x.alpha = -1.0f; x.beta = 0.0f; x.transB = 0; x.flags = kALower;
-      return gemm_f32(x, stream);
-    };
-    gptq_status st;
-    if (full > 0 && (st = pair(0, h, full, T)) != GPTQ_OK) return st;
-    // the T of the ragged group sits after those of the full groups
-    if (tail > hb && (st = pair(full * 2 * hb, (tail - hb) * NB, 1, T + static_cast<int64_t>(full) * h * h)) != GPTQ_OK)
-      return st;
+  // the rest of the inverse on the main stream, after what the second side stream holds
+  if (tri_forked) {
+    GPTQ_HIP_TRY(hipEventRecord(sc.side->join3, s2));
+    GPTQ_HIP_TRY(hipStreamWaitEvent(s0, sc.side->join3, 0));
   }
-  return GPTQ_OK;
+  return tri.issue(nb, s0, 0);
 }
 
 }  // namespace
@@ -708,10 +769,14 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
     Sched sc{stream, nullptr, d_in / NB, batch};
     gptq_status st = side_stream(&sc.side);
     if (st != GPTQ_OK) return st;
-    st = batch >= kLeftLookingBatch ? chol_left(d_in, w.A, U, bsu, w.Linv, w.flag, d_in / NB, batch, stream)
-                                    : chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc);
+    TriInverse tri{d_in, d_in / NB, batch, U, bsu, w.Linv, w.T};
+    if (batch >= kLeftLookingBatch) {
+      st = chol_left(d_in, w.A, U, bsu, w.Linv, w.flag, d_in / NB, batch, stream);
+      if (st == GPTQ_OK) st = tri.issue(d_in / NB, stream, 0);
+    } else {
+      st = chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc, tri);
+    }
     if (st != GPTQ_OK) return st;
-    if ((st = trtri_doubling(d_in, U, bsu, w.Linv, w.T, d_in / NB, batch, stream)) != GPTQ_OK) return st;
   }
   GPTQ_LAUNCH(reverse_to_upper_kernel, dim3((d_in / 4 + 255) / 256, (d_in + REV_ROWS - 1) / REV_ROWS, batch), blk, 0,
               stream, w.Linv, d_in, U, bsu);
