@@ -638,7 +638,11 @@ gptq_status gemm_f32(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((g.N + T - 1) / T, (g.M + T - 1) / T, nz);
   if (g.role == 1) {   // lazy trailing updates: never transposed
     if (g.transB) return GPTQ_ERR_UNSUPPORTED;
-    if (big && vec4) GPTQ_LAUNCH((gemm_x6_kernel<false, 1>), grid, dim3(256), 0, stream, g);
+    // split-bf16 from half a chip of 128-wide tiles: their K grows with N, and the fp32
+    // kernel's 64-wide tiles take the long-K mid levels at under half the rate (d_in 14336:
+    // N = K = 896 at 96 us; quantize -0.12 ms)
+    if (vec4 && tiles128 >= 128)
+      GPTQ_LAUNCH((gemm_x6_kernel<false, 1>), dim3((g.N + 127) / 128, (g.M + 127) / 128, nz), dim3(256), 0, stream, g);
     else if (big) GPTQ_LAUNCH((gemm_f32_kernel<false, 128, false, 1>), grid, dim3(256), 0, stream, g);
     else if (vec4) GPTQ_LAUNCH((gemm_f32_kernel<false, 64, true, 1>), grid, dim3(256), 0, stream, g);
     else GPTQ_LAUNCH((gemm_f32_kernel<false, 64, false, 1>), grid, dim3(256), 0, stream, g);
