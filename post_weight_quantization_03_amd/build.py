@@ -20,7 +20,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq.so")
 
-SOURCES = ["gptq_abi.hip", "hessian.hip", "gemm.hip", "prepare.hip", "quantize.hip", "pack.hip", "serve.hip"]
+# the column sweep's instantiations (sweep_*.hip) are the slowest to compile: first, so
+# that they start at once
+SOURCES = ["sweep_g0.hip", "sweep_g128.hip", "sweep_misc.hip", "quantize.hip", "gptq_abi.hip", "hessian.hip",
+           "gemm.hip", "prepare.hip", "pack.hip", "serve.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 

@@ -13,7 +13,7 @@
 //   static_grid:     static groups only: the grid of every group of original columns,
 //                    fitted on W before the sweep
 //   per block b of 128 columns:
-//     block_sweep:   16 lanes per row keep the row's 128 block columns in registers
+//     block_sweep:   (sweep.h) 16 lanes per row keep the row's 128 block columns in registers
 //                    (8 each); the column value is broadcast within the row by DPP and
 //                    quantized by all 16; U's diagonal block sits in LDS.  Outputs codes
 //                    (processing order), the group scale/zero, and the block's columns
@@ -27,6 +27,7 @@
 #include <utility>
 
 #include "common.h"
+#include "sweep.h"
 
 // Scratch of the allocation-free entry point (gptq_quantize_layer_noalloc): a fixed array
 // of device memory, one per GPU that the library runs on, held until the process ends.
@@ -126,21 +127,6 @@ __global__ __launch_bounds__(256) void inverse_perm_kernel(const int32_t* __rest
   inv[static_cast<int64_t>(e) * d_in + c] = j;
 }
 
-// Grid of one row segment from its range widened to contain 0, [lo, hi] with lo <= 0 <=
-// hi ("GPTQ Architecture, in depth", "The algorithm in code" and "Groups, act-order and
-// other knobs"): asymmetric, step (hi - lo) / maxq and zero level rne(-lo / step); or
-// symmetric, step max|w| / (2^(bits-1) - 1) and zero level fixed at 2^(bits-1) (the grid
-// of "Same Ruler, Smarter Placement: GPTQ", 1.11).  The step is never below 1e-8.
-__device__ __forceinline__ void fit_grid(float lo, float hi, float maxq, bool sym, float& s, float& z) {
-  if (sym) {
-    const float half = 0.5f * (maxq + 1.0f);
-    s = fmaxf(fmaxf(-lo, hi) / (half - 1.0f), 1e-8f);
-    z = half;
-  } else {
-    s = fmaxf((hi - lo) / maxq, 1e-8f);
-    z = rintf(-lo / s);
-  }
-}
 
 // One grid per row, fitted on the whole (dead-zeroed) row at the first column.
 __global__ __launch_bounds__(256) void row_grid_kernel(const float* __restrict__ Wp, int d_out, int d_in,
@@ -200,243 +186,6 @@ __global__ __launch_bounds__(256) void static_grid_kernel(const T* __restrict__ 
   zeros[o] = static_cast<uint8_t>(z);
 }
 
-// A row of W is spread over LPR lanes (16: one DPP row; 4: one DPP quad).  Broadcast of
-// lane `src` of the group, and min / max over the group.
-template <int LPR, int src>
-__device__ __forceinline__ float grp_bcast(float v) {
-  if constexpr (LPR == 16) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + src, 0xF, 0xF, false));
-  else return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), src * 0x55, 0xF, 0xF, false));
-}
-template <int ctrl>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
-}
-// row_ror:n = 0x120 + n; quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E
-template <int LPR>
-__device__ __forceinline__ float grp_min(float v) {
-  if constexpr (LPR == 16) {
-    v = fminf(v, dpp_f<0x128>(v));
-    v = fminf(v, dpp_f<0x124>(v));
-    v = fminf(v, dpp_f<0x122>(v));
-    return fminf(v, dpp_f<0x121>(v));
-  } else {
-    v = fminf(v, dpp_f<0xB1>(v));
-    return fminf(v, dpp_f<0x4E>(v));
-  }
-}
-template <int LPR>
-__device__ __forceinline__ float grp_max(float v) {
-  if constexpr (LPR == 16) {
-    v = fmaxf(v, dpp_f<0x128>(v));
-    v = fmaxf(v, dpp_f<0x124>(v));
-    v = fmaxf(v, dpp_f<0x122>(v));
-    return fmaxf(v, dpp_f<0x121>(v));
-  } else {
-    v = fmaxf(v, dpp_f<0xB1>(v));
-    return fmaxf(v, dpp_f<0x4E>(v));
-  }
-}
-
-// One 128-column block of the sweep.  G = group size (16, 32, 64 or 128), or 0 for the
-// per-row grid already written by row_grid_kernel.  kStatic (with G = 0): every column
-// takes the grid of its original group, perm[column] / gsz, written before the sweep by
-// static_grid_kernel; each lane loads the grids of its own columns once and the column's
-// owner broadcasts them with the column value.  sym selects the symmetric grid at group
-// starts.  NT threads per workgroup, LPR lanes per row of W, so NT / LPR rows per workgroup.
-//
-// Lane k of a row keeps the C = 128 / LPR columns LPR m + k (m = 0..C-1) in registers.
-// For column j the owner lane's value is broadcast to the row's lanes, every lane of the
-// row quantizes it (so all hold err_j and code_j), and each lane updates its own later
-// columns: with the columns interleaved every lane has the same number of them, so the
-// update loop starts at a compile-time index.  Fewer lanes per row repeat the per-column
-// quantization on fewer lanes (4 lanes: a quarter of the instructions per row and column
-// of 16), but need 4x the rows to fill the chip.  The U block sits in LDS as
-// Ul[j][CP k + m] = U[j0 + j][j0 + LPR m + k] with its diagonal zeroed (1/U_jj kept apart):
-// a lane's update reads are contiguous, the rows of a wave read the same words, and
-// columns at or before j get a zero factor.  At a group start the grid is fitted on the
-// row's current values of the group's columns (min/max reduced over the row's lanes).
-template <int G, int NT, int LPR, bool kStatic>
-__global__ __launch_bounds__(NT) void block_sweep_kernel(const float* __restrict__ Wp, const float* __restrict__ U,
-                                                         int64_t bsu, int d_out, int d_in, int blk, float maxq,
-                                                         int sym, const int32_t* __restrict__ perm, int gsz,
-                                                         float* __restrict__ scales, uint8_t* __restrict__ zeros,
-                                                         uint8_t* __restrict__ codes_p, float* __restrict__ err) {
-  constexpr int C = kBlock / LPR;   // columns per lane
-  constexpr int CW = C / 4;         // code words per lane
-  constexpr int CQ = C / 4;         // float4 of a U row per lane
-  // a lane's slice of a U row in LDS: padded at 4 lanes per row, so that the four lanes'
-  // 16-byte reads start on different banks (unpadded, 32 floats apart, they collide)
-  constexpr int CP = LPR == 4 ? C + 4 : C;
-  constexpr int UR = LPR * CP;      // floats per staged U row
-  static_assert(G == 0 || G % LPR == 0, "a group spans whole registers");
-  static_assert(!kStatic || G == 0, "static groups are fitted before the sweep");
-  __shared__ __attribute__((aligned(16))) float Ul[kBlock * UR];
-  __shared__ float inv_d[kBlock];
-  const int e = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int j0 = blk * kBlock;
-  const float* Ub = U + static_cast<int64_t>(e) * bsu + static_cast<int64_t>(j0) * d_in + j0;
-  const int r = blockIdx.x * (NT / LPR) + tid / LPR;
-  const int k = tid % LPR;
-  const bool live = r < d_out;
-  // the row's block columns are fetched first, so they arrive while U is staged
-  const float* wrow = Wp + (static_cast<int64_t>(e) * d_out + (live ? r : 0)) * d_in + j0;
-  float w[C];
-#pragma unroll
-  for (int m = 0; m < C; ++m) w[m] = wrow[LPR * m + k];
-  // stage the U block: item i = (row j, lane kk) gathers U[j][LPR m + kk], m = 0..C-1 (each
-  // load instruction reads LPR consecutive floats per row) and writes them as C
-  // consecutive floats.  A thread's items are all loaded before any is stored, so their
-  // loads overlap (one item at a time left the block's 64 KB as SI serial load latencies).
-  constexpr int ITEMS = kBlock * LPR;
-  constexpr int SI = (ITEMS + NT - 1) / NT;   // items per thread
-  {
-    float v[SI][C];
-#pragma unroll
-    for (int s = 0; s < SI; ++s) {
-      const int i = tid + s * NT;
-      if (ITEMS % NT == 0 || i < ITEMS) {
-        const float* src = Ub + static_cast<int64_t>(i / LPR) * d_in + i % LPR;
-#pragma unroll
-        for (int m = 0; m < C; ++m) v[s][m] = src[LPR * m];
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < SI; ++s) {
-      const int i = tid + s * NT;
-      if (ITEMS % NT == 0 || i < ITEMS) {
-        const int j = i / LPR, kk = i % LPR;
-#pragma unroll
-        for (int m = 0; m < C; ++m) {
-          if (LPR * m + kk == j) {
-            inv_d[j] = 1.0f / v[s][m];
-            v[s][m] = 0.0f;
-          }
-        }
-        float4* dst = reinterpret_cast<float4*>(Ul + j * UR + CP * kk);
-#pragma unroll
-        for (int q = 0; q < CQ; ++q)
-          dst[q] = make_float4(v[s][4 * q], v[s][4 * q + 1], v[s][4 * q + 2], v[s][4 * q + 3]);
-      }
-    }
-  }
-  __syncthreads();
-  if (!live) return;   // whole rows leave together; no barrier follows
-  const int n_groups = G ? d_in / G : (kStatic ? d_in / gsz : 1);
-  float* sc = scales + static_cast<int64_t>(e) * n_groups * d_out;
-  uint8_t* zr = zeros + static_cast<int64_t>(e) * n_groups * d_out;
-  float s = 1.0f, z = 0.0f, inv_s = 1.0f;
-  // static groups: the grid of each of this lane's columns (scale, 1 / scale, zero)
-  constexpr int CS = kStatic ? C : 1;
-  float g_s[CS], g_is[CS], g_z[CS];
-  if constexpr (kStatic) {
-    const int32_t* pe = perm + static_cast<int64_t>(e) * d_in + j0;
-#pragma unroll
-    for (int m = 0; m < C; ++m) {
-      const int c = min(max(pe[LPR * m + k], 0), d_in - 1);
-      const int64_t o = static_cast<int64_t>(c / gsz) * d_out + r;
-      g_s[m] = sc[o];
-      g_z[m] = static_cast<float>(zr[o]);
-      g_is[m] = 1.0f / g_s[m];
-    }
-  } else if constexpr (G == 0) {
-    s = sc[r];
-    z = static_cast<float>(zr[r]);
-    inv_s = 1.0f / s;
-  }
-  // Codes.  16 lanes per row: the owner of a column keeps its code, as it keeps its error,
-  // and each lane stores the codes of its own columns.  4 lanes per row: lane k packs the
-  // codes of columns C k .. C k + C - 1 (every lane has every code).
-  constexpr bool kOwnCodes = LPR == 16;
-  float qv[kOwnCodes ? C : 1];
-  uint32_t cw[kOwnCodes ? 1 : CW];
-  if constexpr (!kOwnCodes) {
-#pragma unroll
-    for (int q = 0; q < CW; ++q) cw[q] = 0u;
-  }
-  float zmax = maxq - z;   // upper clamp of code - zero for the current group
-  const float* ul_k = Ul + CP * k;
-  // U row j is read into registers one column ahead (two alternating sets), so that the
-  // LDS latency stays off the column-to-column chain
-  float4 ua[CQ], ub[CQ];
-#pragma unroll
-  for (int q = 0; q < CQ; ++q) ua[q] = reinterpret_cast<const float4*>(ul_k)[q];
-  float dja = inv_d[0], djb = 0.0f;
-
-  static_for(std::make_integer_sequence<int, kBlock>{}, [&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int mj = j / LPR;
-    float4* cur = (j & 1) ? ub : ua;
-    float4* nxt = (j & 1) ? ua : ub;
-    const float dj = (j & 1) ? djb : dja;
-    if constexpr (j + 1 < kBlock) {
-      const float4* un = reinterpret_cast<const float4*>(ul_k + (j + 1) * UR);
-      static_for(std::make_integer_sequence<int, CQ>{}, [&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        if constexpr (4 * q + 3 >= (j + 1) / LPR) nxt[q] = un[q];
-      });
-      if constexpr (j & 1) dja = inv_d[j + 1];
-      else djb = inv_d[j + 1];
-      // the scheduler would sink these reads next to their use in the next column
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (G != 0 && j % G == 0) {
-      float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-      for (int m = j / LPR; m < (j + G) / LPR; ++m) {
-        lo = fminf(lo, w[m]);
-        hi = fmaxf(hi, w[m]);
-      }
-      lo = grp_min<LPR>(lo);
-      hi = grp_max<LPR>(hi);
-      fit_grid(lo, hi, maxq, sym != 0, s, z);
-      inv_s = 1.0f / s;
-      zmax = maxq - z;
-      if (k == 0) {
-        const int gi = (j0 + j) / G;
-        sc[static_cast<int64_t>(gi) * d_out + r] = s;
-        zr[static_cast<int64_t>(gi) * d_out + r] = static_cast<uint8_t>(z);
-      }
-    }
-    if constexpr (kStatic) {
-      s = grp_bcast<LPR, j % LPR>(g_s[mj]);
-      inv_s = grp_bcast<LPR, j % LPR>(g_is[mj]);
-      z = grp_bcast<LPR, j % LPR>(g_z[mj]);
-    }
-    const float wj = grp_bcast<LPR, j % LPR>(w[mj]);
-    // t = code - zero: round(w / s) clamped to [-z, maxq - z] (the code clamp(round(w / s)
-    // + z, 0, maxq) less z, exactly), so that the dequantized value is s t and the scaled
-    // error (w - s t) / U_jj takes one fused multiply-add and a multiply
-    const float zq = kStatic ? maxq - z : zmax;
-    const float t = __builtin_amdgcn_fmed3f(rintf(wj * inv_s), -z, zq);
-    const float e_j = fmaf(-s, t, wj) * dj;
-    const float q = t + z;
-    if constexpr (kOwnCodes) {
-      if (k == j % LPR) qv[mj] = q;   // the owner keeps the code of its column
-    } else {
-      cw[(j % C) / 4] |= (k == j / C) ? (static_cast<uint32_t>(q) << (8 * (j & 3))) : 0u;
-    }
-#pragma unroll
-    for (int m = mj; m < C; ++m) {
-      const float4 u4 = cur[m / 4];
-      const float u = (m & 3) == 0 ? u4.x : (m & 3) == 1 ? u4.y : (m & 3) == 2 ? u4.z : u4.w;
-      w[m] = fmaf(-e_j, u, w[m]);
-    }
-    if (k == j % LPR) w[mj] = e_j;   // the owner keeps err_j in place of w_j
-  });
-  uint8_t* crow = codes_p + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
-  if constexpr (kOwnCodes) {
-#pragma unroll
-    for (int m = 0; m < C; ++m) crow[LPR * m + k] = static_cast<uint8_t>(qv[m]);
-  } else {
-    uint32_t* cdst = reinterpret_cast<uint32_t*>(crow + C * k);
-#pragma unroll
-    for (int q = 0; q < CW; q += 4) *reinterpret_cast<uint4*>(cdst + q) = make_uint4(cw[q], cw[q + 1], cw[q + 2], cw[q + 3]);
-  }
-  float* edst = err + (static_cast<int64_t>(e) * d_out + r) * d_in + j0;
-#pragma unroll
-  for (int m = 0; m < C; ++m) edst[LPR * m + k] = w[m];
-}
 
 // codes[:, c] = codes_p[:, inv[c]]; g_idx[c] = inv[c] / group.  Staged like the weight
 // permute: inv once per workgroup, each codes_p row in LDS, 16 codes per thread per store.
@@ -517,29 +266,27 @@ QuantWs carve(void* ws, int batch, int d_out, int d_in) {
   return w;
 }
 
-// Launch geometry of the sweep: NT threads per workgroup, LPR lanes per row, the grid.
-struct SweepShape {
-  int nt, lpr;
-  dim3 grid;
-};
-
 // The U block takes 64 KB of LDS, so at most two workgroups share a CU.  With rows enough
 // for about one wave per SIMD at 4 lanes per row (16 rows per wave), rows get 4 lanes;
 // else 16.  At 16 lanes, the largest workgroup that still gives every CU at least one.  At
 // 4 lanes the sweep is bound by VALU issue and LDS reads, so its time goes with the rows
 // the busiest CU takes, ceil(workgroups / 256) x rows per workgroup: of the workgroup sizes
-// below, the one that makes this smallest (64 experts of 1408 rows: 704 threads, 8 x 64
-// workgroups of 176 rows in two even rounds, where 1024 threads left a third of the chip
-// idle in the second round).  Groups of 64 at 4 lanes per row stop at 512 threads (their
-// registers would not fit more).  The small groups (16, 32) keep 16 lanes and 256
-// threads: their sweeps need too many registers for more than one wave per SIMD.
+// below, with one or two rows per lane, the one that makes this smallest, a lane's second
+// row counted as half a row (it shares the lane's U reads and loop overhead).  64 experts
+// of 1408 rows: 704 threads with two rows per lane, one workgroup of 352 rows per CU
+// (sweep 74 -> 55 us against two rounds of 176 rows at one row per lane, where 1024
+// threads at one row left a third of the chip idle in the second round); 14336 rows: one
+// row per lane (two would leave half the SIMDs without a wave).  Groups of 64 at 4 lanes
+// per row stop at 512 threads and one row (their registers would not fit more).  The small
+// groups (16, 32) keep 16 lanes and 256 threads: their sweeps need too many registers for
+// more than one wave per SIMD.
 constexpr int kCUs = 256;
 SweepShape sweep_shape(int G, bool stat, int batch, int d_out) {
   // static groups keep 16 lanes per row: each lane also holds the grids of its columns
   const bool wide_ok = !stat && (G == 0 || G == 64 || G == 128);
   const int64_t rows = static_cast<int64_t>(batch) * d_out;
   const int lpr = (wide_ok && rows / 16 >= 768) ? 4 : 16;
-  int nt = 256;
+  int nt = 256, rpl = 1;
   if (wide_ok && lpr == 16) {
     for (int cand : {1024, 512}) {
       const int rpw = cand / lpr;
@@ -549,73 +296,30 @@ SweepShape sweep_shape(int G, bool stat, int batch, int d_out) {
       }
     }
   } else if (wide_ok) {
+    // cost in row-steps of the busiest CU; a lane's second row costs half a row (4 x the
+    // cost compared against 3 x for two rows per lane)
     int64_t best = -1;
-    for (int cand : {1024, 704, 512, 256}) {
-      if (G == 64 && cand > 512) continue;   // would spill registers
-      const int rpw = cand / lpr;
-      const int64_t wgs = static_cast<int64_t>((d_out + rpw - 1) / rpw) * batch;
-      const int64_t cost = (wgs + kCUs - 1) / kCUs * rpw;
-      if (best < 0 || cost < best) {
-        best = cost;
-        nt = cand;
+    for (int two = 0; two < 2; ++two) {
+      if (two && G == 64) continue;   // would spill registers
+      for (int cand : {1024, 704, 512, 256}) {
+        if ((G == 64 || two) && cand > 512 + 192 * two) continue;   // would spill registers
+        const int rpw = cand / lpr * (two + 1);
+        const int64_t wgs = static_cast<int64_t>((d_out + rpw - 1) / rpw) * batch;
+        const int64_t cost = (wgs + kCUs - 1) / kCUs * rpw * (two ? 3 : 4);
+        if (best < 0 || cost < best) {
+          best = cost;
+          nt = cand;
+          rpl = two + 1;
+        }
       }
     }
   }
-  const int rpw = nt / lpr;
-  return {nt, lpr, dim3((d_out + rpw - 1) / rpw, batch)};
-}
-
-// Arguments of every sweep launch of one quantize call.
-struct SweepArgs {
-  const float* Wp;
-  const float* U;
-  int64_t bsu;
-  int d_out, d_in;
-  float maxq;
-  int sym;
-  const int32_t* perm;   // static groups: processing position -> original column
-  int gsz;               // static groups: group size
-  float* scales;
-  uint8_t* zeros;
-  uint8_t* codes_p;
-  float* err;
-  bool timed;            // the launch-timing hook may bracket these launches
-};
-
-template <int G, int NT, int LPR, bool kStatic>
-gptq_status launch_sweep(dim3 grid, hipStream_t stream, const SweepArgs& a, int blk) {
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (a.timed) timing_pair(GPTQ_TIME_SWEEP, &ev0, &ev1);
-  if (ev0) GPTQ_HIP_TRY(hipEventRecord(ev0, stream));
-  GPTQ_LAUNCH((block_sweep_kernel<G, NT, LPR, kStatic>), grid, dim3(NT), 0, stream, a.Wp, a.U, a.bsu, a.d_out, a.d_in,
-              blk, a.maxq, a.sym, a.perm, a.gsz, a.scales, a.zeros, a.codes_p, a.err);
-  if (ev1) GPTQ_HIP_TRY(hipEventRecord(ev1, stream));
-  return GPTQ_OK;
-}
-
-template <int G>
-gptq_status launch_sweep_nt(const SweepShape& sh, hipStream_t stream, const SweepArgs& a, int blk) {
-  if constexpr (G == 0 || G == 64 || G == 128) {
-#define GPTQ_SWEEP(NT, LPR) \
-  if (sh.nt == NT && sh.lpr == LPR) return launch_sweep<G, NT, LPR, false>(sh.grid, stream, a, blk);
-    GPTQ_SWEEP(512, 16)   // 1024 threads at 16 lanes: never chosen (4 lanes take over first)
-    if constexpr (G != 64) {
-      GPTQ_SWEEP(1024, 4)
-      GPTQ_SWEEP(704, 4)
-    }
-    GPTQ_SWEEP(512, 4)
-    GPTQ_SWEEP(256, 4)
-#undef GPTQ_SWEEP
-  }
-  if (sh.nt != 256 || sh.lpr != 16) return GPTQ_ERR_UNSUPPORTED;
-  return launch_sweep<G, 256, 16, false>(sh.grid, stream, a, blk);
+  const int rpw = nt / lpr * rpl;
+  return {nt, lpr, rpl, dim3((d_out + rpw - 1) / rpw, batch)};
 }
 
 gptq_status sweep_block(int b, int G, bool stat, const SweepShape& sg, hipStream_t stream, const SweepArgs& a) {
-  if (stat) {
-    if (sg.nt != 256 || sg.lpr != 16) return GPTQ_ERR_UNSUPPORTED;
-    return launch_sweep<0, 256, 16, true>(sg.grid, stream, a, b);
-  }
+  if (stat) return launch_sweep_static(sg, stream, a, b);
   switch (G) {
     case 0: return launch_sweep_nt<0>(sg, stream, a, b);
     case 16: return launch_sweep_nt<16>(sg, stream, a, b);

@@ -48,13 +48,20 @@ CASES = {
     "per_row_4_lanes": synth.scaled("moe", d_out=520, d_in=256, n_tokens=600, batch=24, seq_len=300,
                                     group_size=-1),
     "group128_4_lanes_512": synth.scaled("moe", d_out=512, d_in=128, n_tokens=400, batch=64, seq_len=200),
-    # 704 threads at 4 lanes per row (176 rows per workgroup, 8 x 32 = 256 workgroups: the
-    # shape that evens out the busiest CU's rows), with groups and with one grid per row
+    # (the shape per case follows the sweep's cost rule: threads per workgroup, rows per lane)
+    # 704 threads at 4 lanes per row, one row per lane (176 rows per workgroup, 8 x 32 = 256
+    # workgroups), with groups and with one grid per row
     "group128_4_lanes_704": synth.scaled("moe", d_out=1408, d_in=256, n_tokens=300, batch=32, seq_len=300),
     "per_row_4_lanes_704": synth.scaled("moe", d_out=1408, d_in=256, n_tokens=300, batch=32, seq_len=300,
                                         group_size=-1),
-    # 1024 threads at 4 lanes per row (4 x 64 = 256 workgroups of 256 rows)
+    # 512 threads at 4 lanes per row, two rows per lane (4 x 64 = 256 workgroups of 256 rows)
     "group128_4_lanes_1024": synth.scaled("moe", d_out=1024, d_in=128, n_tokens=300, batch=64, seq_len=300),
+    # 704 threads, two rows per lane (352 rows per workgroup, 4 x 64 workgroups), the last
+    # workgroup of each expert ragged: its second pass partly past d_out (1300 rows), or its
+    # first pass partly and its second wholly (1100 rows, one grid per row)
+    "group128_4_lanes_2rows_704": synth.scaled("moe", d_out=1300, d_in=256, n_tokens=300, batch=64, seq_len=300),
+    "per_row_4_lanes_2rows_704": synth.scaled("moe", d_out=1100, d_in=256, n_tokens=300, batch=64, seq_len=300,
+                                              group_size=-1),
     # fp16 inputs (the f16 matrix-core SYRK, fp16 channel energies and weight permutes)
     "fp16_attn_scaled": synth.scaled("attn_proj", d_out=136, d_in=384, n_tokens=3000, seq_len=1000, dtype="f16"),
     "fp16_moe_scaled": synth.scaled("moe", d_out=64, d_in=256, n_tokens=900, batch=3, seq_len=300, dtype="f16",
