@@ -136,10 +136,10 @@ struct ServeArgs {
 };
 
 // One workgroup: 256 consecutive outputs (64 per wave), one K chunk of at most SV_KMAX
-// inputs, 16 activation rows (blockIdx.z selects the pass).  Every lane first issues the
-// loads of all its qweight vectors of the chunk (one 16-byte vector per 32-input step: 4
+// inputs, 16 activation rows (blockIdx.z selects the pass).  Every lane issues the loads
+// of all its qweight vectors of the chunk (one 16-byte vector per 32-input step: 4
 // consecutive outputs of one 8-input row), so a wave keeps up to 16 KB of weights in
-// flight; meanwhile the chunk's activations are gathered into LDS in serving order (rows
+// flight, and meanwhile all of the activations it gathers into LDS in serving order (rows
 // past m are zero).  Each step turns the 4 words of its vector into the B operands of 4
 // MFMAs against the same activations, and a fifth MFMA against ones adds the activation
 // sums.  Lane l owns outputs o0 + 4 (l % 16) + t, t = 0..3; after every SEG inputs (a
@@ -162,6 +162,19 @@ __global__ __launch_bounds__(256) void w4a16_kernel(ServeArgs a) {
   const int obc = live ? ob : 0;
   const uint4* qw = reinterpret_cast<const uint4*>(a.qweight + obc);
   const int64_t row4 = a.d_out / 4;           // uint4 per qweight row
+
+  // Loads in three waves, ordered for the wave's in-order memory counter: the serving-order
+  // indices of the thread's two chunk inputs k = tid, tid + 256 first, then the weights and
+  // grids, then the activations at those indices, which wait only for the indices while
+  // the weights are in flight (loaded after the weights, the gather waited for all of them,
+  // and one pass of 16 rows went through it in serial batches)
+  static_assert(SV_KMAX <= 2 * 256, "two chunk inputs per thread");
+  int kc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = tid + 256 * h;
+    kc[h] = k >= kn ? -1 : a.order ? min(max(a.order[k0 + k], 0), a.d_in - 1) : k0 + k;
+  }
   // step i covers inputs k0 + 32 i + 8 q .. + 7: qweight row k0 / 8 + 4 i + q
   uint4 w[NSEG * NS];
 #pragma unroll
@@ -178,18 +191,19 @@ __global__ __launch_bounds__(256) void w4a16_kernel(ServeArgs a) {
       zw[sg] = static_cast<uint32_t>(a.qzeros[static_cast<int64_t>(g) * (a.d_out / 8) + obc / 8]);
     }
   }
-
-  // stage the activations: element (r, k) = X[m0 + r][order[k0 + k]], zero past m; the
-  // gather's index loads of a thread are independent of each other (unrolled)
+  // the activations: element (r, k) = X[m0 + r][order[k0 + k]], zero for rows past m
   const int mrows = min(SV_M, a.m - m0);
-#pragma unroll 4
-  for (int i = tid; i < mrows * kn; i += 256) {
-    const int r = i / kn, k = i - r * kn;
-    const int c = a.order ? min(max(a.order[k0 + k], 0), a.d_in - 1) : k0 + k;
-    xs[r * LDX + k] = a.X[static_cast<int64_t>(m0 + r) * a.ldx + c];
-  }
-  for (int i = tid; i < (SV_M - mrows) * (LDX / 8); i += 256)
-    reinterpret_cast<uint4*>(xs + mrows * LDX)[i] = make_uint4(0u, 0u, 0u, 0u);
+  uint16_t xv[SV_M][2];
+#pragma unroll
+  for (int r = 0; r < SV_M; ++r)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      xv[r][h] = (r < mrows && kc[h] >= 0) ? a.X[static_cast<int64_t>(m0 + r) * a.ldx + kc[h]] : uint16_t{0};
+#pragma unroll
+  for (int r = 0; r < SV_M; ++r)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (kc[h] >= 0) xs[r * LDX + tid + 256 * h] = xv[r][h];
   __syncthreads();
 
   const s16x8 ones = kBF16 ? s16x8{0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80}
