@@ -468,6 +468,30 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   const int64_t tstride = static_cast<int64_t>(ST) * ST;
   const int64_t kstride = static_cast<int64_t>(ntiles) * tstride;
   const float* P0 = partial + (static_cast<int64_t>(e) * nsplit * ntiles + tile) * tstride + sm * ST + sn + c4;
+  // The old values of H under the sub-block and under its mirror are loaded first, so that
+  // their latency overlaps the partials' (after the sum, one read-modify-write and then the
+  // other put two more latencies on every workgroup).  Each element of H belongs to one
+  // sub-block, as lower value or as mirror, so no other workgroup writes what these read.
+  // The four columns of a thread's row take one 16-byte read-modify-write where all four
+  // are inside H and on or below the diagonal (and H's rows are 16-byte aligned).
+  const bool vec_rows = (d_in % 4 == 0) && (reinterpret_cast<uintptr_t>(He) % 16 == 0);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  float4 hlo[4];
+  bool hvec[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = sm + r0 + 16 * q;
+    const int row = I * ST + m, col0 = J * ST + sn + c4;
+    hvec[q] = vec_rows && row < d_in && col0 + 3 < d_in && (!diag || m >= sn + c4 + 3);
+    if (hvec[q]) hlo[q] = *reinterpret_cast<const float4*>(He + static_cast<int64_t>(row) * d_in + col0);
+  }
+  float hmir[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int n = sn + ty + 4 * u, m = sm + tx;   // element (m, n) of the tile
+    const int row = I * ST + m, col = J * ST + n;
+    hmir[u] = (row < d_in && col < d_in && (!diag || m > n)) ? He[static_cast<int64_t>(col) * d_in + row] : 0.0f;
+  }
   float4 acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -479,9 +503,6 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
       acc[q].x += v.x; acc[q].y += v.y; acc[q].z += v.z; acc[q].w += v.w;
     }
   }
-  // the four columns of a thread's row are added with one 16-byte read-modify-write where
-  // all four are inside H and on or below the diagonal (and H's rows are 16-byte aligned)
-  const bool vec_rows = (d_in % 4 == 0) && (reinterpret_cast<uintptr_t>(He) % 16 == 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int i = r0 + 16 * q, m = sm + i;
@@ -489,11 +510,10 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 #pragma unroll
     for (int t = 0; t < 4; ++t) tr[i][c4 + t] = v[t];
     const int row = I * ST + m, col0 = J * ST + sn + c4;
-    if (vec_rows && row < d_in && col0 + 3 < d_in && (!diag || m >= sn + c4 + 3)) {
-      float4* h = reinterpret_cast<float4*>(He + static_cast<int64_t>(row) * d_in + col0);
-      float4 o = *h;
+    if (hvec[q]) {
+      float4 o = hlo[q];
       o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
-      *h = o;
+      *reinterpret_cast<float4*>(He + static_cast<int64_t>(row) * d_in + col0) = o;
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -505,12 +525,13 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   }
   __syncthreads();
   // mirror: H[col][row] for the same sub-block, written along rows of the transpose
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int i = ty + 4 * u;
     const int n = sn + i, m = sm + tx;       // element (m, n) of the tile
     const int row = I * ST + m, col = J * ST + n;
     if (row < d_in && col < d_in && (!diag || m > n))
-      He[static_cast<int64_t>(col) * d_in + row] += tr[tx][i];
+      He[static_cast<int64_t>(col) * d_in + row] = hmir[u] + tr[tx][i];
   }
 }
 
