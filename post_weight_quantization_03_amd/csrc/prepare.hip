@@ -631,7 +631,7 @@ int far_group(int nb) { return nb <= 32 ? 2 : 4; }
 // every CU (three workgroups each), a far update holds each chain kernel issued during it
 // until it has finished (d_in 4096: prepare 2.59 -> 2.51 ms when limited).  Wider layers keep
 // the full-chip far updates: one workgroup per CU runs their long updates 1.5x slower, more
-// than the chain gains (d_in 14336: prepare 19.5 -> 21.4 ms when limited).
+// than the chain gains (d_in 14336: prepare 17.9 -> 18.4 ms when limited).
 constexpr int kFarCUs = 240;
 int far_cus(int nb) { return nb <= 32 ? kFarCUs : 0; }
 
