@@ -162,6 +162,11 @@ gptq_status gptq_accumulate_hessian_grouped(int batch, int d_in, int64_t total_t
  * chol route.  Returns GPTQ_ERR_NOT_SPD (after waiting for the stream) when a pivot is
  * not positive or not finite; the caller may retry with a larger damp.
  * Requires d_in % 128 == 0.
+ * For one to three problems per call, parts of the factorisation and of the inverse run
+ * on two streams that the library creates per device (kept for the life of the process),
+ * forked from `stream` with events and joined back into it before the call returns; where
+ * the process's other streams already hold the device's hardware queues, those parts run
+ * serialized with the rest and take longer, with the same results.
  */
 gptq_status gptq_prepare_hinv(int batch, int d_in, const float* H, int64_t batch_stride_h,
                               const double* diag_key, const gptq_params* p, float* U,
