@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void damping_kernel(const double* __restrict__
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
   if (threadIdx.x == 0) {
@@ -568,8 +568,14 @@ struct TriInverse {
 // matrix once per G panels (with K = 128 these updates are bound by that traffic); the near
 // updates then carry K = 2..G+1 panels.  Every block receives the updates of all earlier
 // panels exactly once before it is factored.
-// From this many problems per call on, the Cholesky runs left-looking on one stream.
+// From this many problems per call on, the Cholesky runs left-looking (chol_left).
 constexpr int kLeftLookingBatch = 4;
+
+// Block columns between the points where the triangular inverse's ready products are
+// enqueued beside the factorization, and the CUs they may take there (0: all).
+constexpr int kTriStep = 8;
+constexpr int kTriMaxHb = 1 << 30;
+int tri_cus(int nb) { return 0; }
 
 struct Sched {
   hipStream_t main;
@@ -581,14 +587,19 @@ float* block_at(float* base, int d_in, int bi, int bj) {
   return base + static_cast<int64_t>(bi) * NB * d_in + static_cast<int64_t>(bj) * NB;
 }
 
-// Left-looking variant for many problems at once, on one stream: block column k first
-// takes the contributions of all earlier columns in one product,
+// Left-looking variant for many problems at once: block column k first takes the
+// contributions of all earlier columns in one product,
 //   A[k:, k] -= L[k:, :k] L[k, :k]^T   (K = 128 k),
 // then the leaf factors its diagonal block and the panel solve gives L[k+1:, k].  With a
-// batch of problems every step already fills the chip, and the trailing matrix is not
-// read and written back once per block column as in the right-looking order.
-gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, int nb, int batch,
-                      hipStream_t s0) {
+// batch of problems the early steps already fill the chip, and the trailing matrix is not
+// read and written back once per block column as in the right-looking order.  The later
+// steps cover fewer and fewer rows, and the inverse's products over the columns already
+// factored run beside them on the second side stream.
+gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc,
+                      TriInverse& tri) {
+  const int nb = sc.nb, batch = sc.batch;
+  hipStream_t s0 = sc.main, s2 = sc.side->s2;
+  bool tri_forked = false;
   const int64_t dd = static_cast<int64_t>(d_in) * d_in;
   for (int k = 0; k < nb; ++k) {
     gptq_status st;
@@ -613,8 +624,20 @@ gptq_status chol_left(int d_in, float* A, float* L, int64_t bsl, float* Linv, in
     g.C = block_at(L, d_in, k + 1, k); g.ldc = d_in; g.sC = bsl;
     g.alpha = 1.0f; g.beta = 0.0f; g.transB = 1; g.flags = kBtLower;
     if ((st = gemm_f32(g, s0)) != GPTQ_OK) return st;
+    // columns 0..k of L are final: the inverse's products over them beside the later steps,
+    // whose products shrink with the columns left
+    if ((k + 1) % kTriStep == 0) {
+      GPTQ_HIP_TRY(hipEventRecord(sc.side->fork2, s0));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(s2, sc.side->fork2, 0));
+      if ((st = tri.issue(k + 1, s2, 0)) != GPTQ_OK) return st;
+      tri_forked = true;
+    }
   }
-  return GPTQ_OK;
+  if (tri_forked) {
+    GPTQ_HIP_TRY(hipEventRecord(sc.side->join3, s2));
+    GPTQ_HIP_TRY(hipStreamWaitEvent(s0, sc.side->join3, 0));
+  }
+  return tri.issue(nb, s0, 0);
 }
 
 // Panels per far update.  While the chain of small products is the critical path (d_in <=
@@ -635,11 +658,6 @@ int far_group(int nb) { return nb <= 32 ? 2 : 4; }
 constexpr int kFarCUs = 240;
 int far_cus(int nb) { return nb <= 32 ? kFarCUs : 0; }
 
-// Block columns between the points where the triangular inverse's ready products are
-// enqueued beside the factorization, and the CUs they may take there (0: all).
-constexpr int kTriStep = 8;
-constexpr int kTriMaxHb = 1 << 30;
-int tri_cus(int nb) { return 0; }
 
 gptq_status chol_blocked(int d_in, float* A, float* L, int64_t bsl, float* Linv, int* flag, const Sched& sc,
                          TriInverse& tri) {
@@ -770,12 +788,8 @@ gptq_status prepare_enqueue(int batch, int d_in, const float* H, int64_t bsh, co
     gptq_status st = side_stream(&sc.side);
     if (st != GPTQ_OK) return st;
     TriInverse tri{d_in, d_in / NB, batch, U, bsu, w.Linv, w.T};
-    if (batch >= kLeftLookingBatch) {
-      st = chol_left(d_in, w.A, U, bsu, w.Linv, w.flag, d_in / NB, batch, stream);
-      if (st == GPTQ_OK) st = tri.issue(d_in / NB, stream, 0);
-    } else {
-      st = chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc, tri);
-    }
+    st = batch >= kLeftLookingBatch ? chol_left(d_in, w.A, U, bsu, w.Linv, w.flag, sc, tri)
+                                    : chol_blocked(d_in, w.A, U, bsu, w.Linv, w.flag, sc, tri);
     if (st != GPTQ_OK) return st;
   }
   GPTQ_LAUNCH(reverse_to_upper_kernel, dim3((d_in / 4 + 255) / 256, (d_in + REV_ROWS - 1) / REV_ROWS, batch), blk, 0,
