@@ -251,21 +251,22 @@ __global__ __launch_bounds__(256) void w4a16_kernel(ServeArgs a) {
 
 __global__ void clear_flag_kernel(int* __restrict__ flag) { *flag = 0; }
 
-// Y[m][o] = sum over chunks of the partials, in chunk order.  The loads of 8 chunks are
-// issued together before they are added (one load after another would put every load's
-// latency on the chain).
+// Y[m][o] = sum over chunks of the partials, in chunk order.  The loads of up to 32 chunks
+// are issued together before they are added (one load after another would put every
+// load's latency on the chain; 8 at a time left a decode call's 28 chunks four latencies).
 __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float* __restrict__ part, int chunks, int m,
                                                            int d_out, float* __restrict__ Y, int64_t ldy) {
+  constexpr int B = 32;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t n = static_cast<int64_t>(m) * d_out;
   if (i >= n) return;
   float s = 0.0f;
-  for (int c0 = 0; c0 < chunks; c0 += 8) {
-    float v[8];
+  for (int c0 = 0; c0 < chunks; c0 += B) {
+    float v[B];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = c0 + c < chunks ? part[static_cast<int64_t>(c0 + c) * n + i] : 0.0f;
+    for (int c = 0; c < B; ++c) v[c] = c0 + c < chunks ? part[static_cast<int64_t>(c0 + c) * n + i] : 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s += v[c];
+    for (int c = 0; c < B; ++c) s += v[c];
   }
   const int64_t r = i / d_out, o = i - r * d_out;
   Y[r * ldy + o] = s;
