@@ -73,6 +73,12 @@ CASES = {
                                           group_size=-1, sym=True),
     "sym_g32_3bit": synth.scaled("mlp_down", d_out=72, d_in=256, n_tokens=1500, seq_len=500, group_size=32, bits=3,
                                  sym=True),
+    # the same grids at 4 lanes per row: two rows per lane (1300 rows x 64, ragged last
+    # workgroups), and groups of 64 (one row per lane, at most 512 threads)
+    "sym_g128_4_lanes_2rows": synth.scaled("moe", d_out=1300, d_in=256, n_tokens=300, batch=64, seq_len=300,
+                                           sym=True),
+    "group64_4_lanes": synth.scaled("moe", d_out=1000, d_in=256, n_tokens=300, batch=16, seq_len=300,
+                                    group_size=64),
     "static_g128_actorder": synth.scaled("attn_proj", d_out=136, d_in=512, n_tokens=4000, seq_len=1000,
                                          static_groups=True),
     "static_g16_sym_f32": synth.scaled("attn_proj", d_out=40, d_in=384, n_tokens=1500, seq_len=500, group_size=16,
