@@ -87,6 +87,12 @@ CASES = {
                                              group_size=64, static_groups=True),
     "static_no_actorder": synth.scaled("mlp_up", d_out=96, d_in=256, n_tokens=1200, seq_len=600,
                                        static_groups=True),
+    # the triangular inverse enqueued beside the factorization (every 8 block columns): 13
+    # block columns (ragged doubling groups at two levels), 10 for a batch of two (the blocked
+    # Cholesky) and for a batch of four (the left-looking one)
+    "inverse_13_blocks": synth.scaled("attn_proj", d_out=64, d_in=1664, n_tokens=4000, seq_len=1000),
+    "inverse_10_blocks_batch2": synth.scaled("moe", d_out=64, d_in=1280, n_tokens=3000, batch=2, seq_len=1000),
+    "inverse_10_blocks_batch4": synth.scaled("moe", d_out=64, d_in=1280, n_tokens=3000, batch=4, seq_len=1000),
     # 36 block columns: the Cholesky's far updates grouped four panels at a time; lazy updates,
     # trailing updates and the triangular inverse large enough for the split-bf16 products
     # (ragged row tiles: 1944 = 15 x 128 + 24; both B layouts; lower-only output)
